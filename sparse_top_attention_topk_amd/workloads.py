@@ -1,0 +1,264 @@
+"""Seeded synthetic problems for sparse top-k MLA attention.
+
+This module only draws inputs: random tensors, index lists and lengths.  It
+holds none of the attention arithmetic, and both the GPU library's callers and
+the CPU oracle consume the same bit patterns from it.
+
+Recipe (fixed generation order per problem): q, kv, dO as fp32 N(0, 1) from
+``numpy.random.default_rng(seed)`` rounded to bf16 (round to nearest even, by
+torch), then the sink (fp32 N(0, 1)), then the indices.  Index lists are int32
+in sampled (unsorted) order.
+
+Shapes follow the workloads of the pages: DeepSeek-V4-like sliding window of
+128 recent positions followed by causal top-k slots, -1 padded
+([flash-attn #2882] Performance at DeepSeek-V4 shapes; the [window | compressed]
+slot order of [cuDNN-FE #298]); compact layouts with a length per token and
+non-compact layouts wider than S_kv ([cuDNN-FE #785] Testing; [cuDNN-FE #298]);
+saturating sinks ([cuDNN-FE #785] Summary 3).  They stand in for the indexer
+output of a trained model, which is not available.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["Problem", "make_problem", "PROBLEMS", "EDGE_HEADS"]
+
+EDGE_HEADS = (1, 24, 64, 96, 128)
+
+
+@dataclass
+class Problem:
+    name: str
+    T: int
+    S_kv: int
+    H: int
+    d_qk: int
+    d_v: int
+    W: int
+    scale: float
+    q: torch.Tensor                      # bf16 [T, H, d_qk] (CPU)
+    kv: torch.Tensor                     # bf16 [S_kv, d_qk]
+    dO: torch.Tensor                     # bf16 [T, H, d_v]
+    topk_idxs: torch.Tensor              # int32 [T, W]
+    topk_length: Optional[torch.Tensor]  # int32 [T] or None
+    attn_sink: Optional[torch.Tensor]    # fp32 [H] or None
+    meta: dict = field(default_factory=dict)
+
+    # fp64 NumPy views of the exact values, for the oracle
+    def np_inputs(self):
+        return dict(
+            q=self.q.double().numpy(),
+            kv=self.kv.double().numpy(),
+            dO=self.dO.double().numpy(),
+            topk_idxs=self.topk_idxs.numpy(),
+            topk_length=None if self.topk_length is None else self.topk_length.numpy(),
+            attn_sink=None if self.attn_sink is None else self.attn_sink.double().numpy(),
+            scale=self.scale,
+            d_v=self.d_v,
+        )
+
+    def valid_count(self) -> int:
+        """Number of valid (token, slot) pairs (the FLOP convention's K summed)."""
+        idx = self.topk_idxs.numpy()
+        ok = (idx >= 0) & (idx < self.S_kv)
+        if self.topk_length is not None:
+            ln = np.clip(self.topk_length.numpy().astype(np.int64), 0, self.W)
+            ok &= np.arange(self.W)[None, :] < ln[:, None]
+        return int(ok.sum())
+
+
+def _bf16(rng, shape):
+    a = rng.standard_normal(size=shape, dtype=np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16)
+
+
+def _dense(rng, T, S_kv, H, d_qk, d_v, with_sink):
+    q = _bf16(rng, (T, H, d_qk))
+    kv = _bf16(rng, (S_kv, d_qk))
+    dO = _bf16(rng, (T, H, d_v))
+    sink = None
+    if with_sink:
+        sink = torch.from_numpy(rng.standard_normal(size=(H,), dtype=np.float32))
+    return q, kv, dO, sink
+
+
+def _causal_tiny_idxs(rng, T, W):
+    """Row t: min(W, t+1) distinct indices drawn from [0, t], then -1."""
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = min(W, t + 1)
+        idx[t, :n] = rng.choice(t + 1, size=n, replace=False)
+    return idx
+
+
+def _window_topk_idxs(rng, T, window, topk):
+    """[window | top-k] rows: slots [0, window) hold max(0,t-window+1)..t
+    ascending then -1; slots [window, window+topk) hold min(topk, t-window+1)
+    distinct indices from [0, t-window] (the causal prefix before the window),
+    then -1."""
+    W = window + topk
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        lo = max(0, t - window + 1)
+        idx[t, : t - lo + 1] = np.arange(lo, t + 1, dtype=np.int32)
+        n_before = lo  # positions 0 .. lo-1 lie before the window
+        k = min(topk, n_before)
+        if k > 0:
+            idx[t, window: window + k] = rng.choice(n_before, size=k, replace=False)
+    return idx
+
+
+def make_tiny(seed=0, sink=True, compact=False):
+    """T=64, S_kv=64 causal, H=4, d_qk=576, d_v=512, width 32, scale 1/sqrt(576)."""
+    rng = np.random.default_rng(seed)
+    T, S, H, dqk, dv, W = 64, 64, 4, 576, 512, 32
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, sink)
+    idx = _causal_tiny_idxs(rng, T, W)
+    length = None
+    if compact:
+        length = torch.from_numpy((idx >= 0).sum(axis=1).astype(np.int32))
+    return Problem("tiny", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), length, s,
+                   meta=dict(seed=seed, compact=compact, sink=sink))
+
+
+def make_edge_compact(H, seed=None):
+    """Compact layout: T=128, S_kv=128, width 64, length ~ U{0..64} with 10% of
+    rows forced to 0; slots < length hold distinct indices from [0,128); the
+    tail holds random in-range indices that must be ignored by position."""
+    if seed is None:
+        seed = 10 + EDGE_HEADS.index(H)
+    rng = np.random.default_rng(seed)
+    T, S, dqk, dv, W = 128, 128, 576, 512, 64
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+    length = rng.integers(0, W + 1, size=T).astype(np.int32)
+    zero = rng.random(T) < 0.10
+    length[zero] = 0
+    length[0] = 0          # at least one empty row, next to a full one
+    length[1] = W
+    idx = rng.integers(0, S, size=(T, W)).astype(np.int32)   # tail: in-range garbage
+    for t in range(T):
+        n = int(length[t])
+        idx[t, :n] = rng.choice(S, size=n, replace=False)
+    return Problem(f"edge_compact_h{H}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk),
+                   q, kv, dO, torch.from_numpy(idx), torch.from_numpy(length), s,
+                   meta=dict(seed=seed))
+
+
+def make_edge_wide(H, seed=None, T=128, S=256, W=1024):
+    """Non-compact layout wider than S_kv: W=1024 > S_kv=256; n_valid[t] ~
+    U{0..256} distinct indices at random slot positions, -1 elsewhere; one row
+    with 0 valid and one with 256.  No sink."""
+    if seed is None:
+        seed = 20 + EDGE_HEADS.index(H)
+    rng = np.random.default_rng(seed)
+    dqk, dv = 576, 512
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, False)
+    nval = rng.integers(0, S + 1, size=T)
+    nval[0] = 0
+    nval[1] = S
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        n = int(nval[t])
+        pos = rng.choice(W, size=n, replace=False)
+        idx[t, pos] = rng.choice(S, size=n, replace=False)
+    return Problem(f"edge_wide_h{H}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk),
+                   q, kv, dO, torch.from_numpy(idx), None, s, meta=dict(seed=seed))
+
+
+SATURATING_SINKS = (3.0e38, -3.0e38, float("inf"), float("-inf"))
+
+
+def make_edge_sink(H, seed=None, sink_cycle_offset=0):
+    """Saturating sinks: T=128, S_kv=128, width 64, causal non-compact;
+    sink[h] = (+3e38, -3e38, +inf, -inf)[(h + offset) mod 4].  Every 4th token
+    (t % 4 == 0) has q scaled by 1e-3; tokens t % 4 == 1 are anti-aligned with
+    their gathered rows so that their scores (and LSE) are strongly negative:
+    q[t,h] = -g * m / |m| with m the sum of the token's gathered kv rows and g
+    chosen so that the largest score is -100 (rows whose projections are not
+    all positive are redrawn)."""
+    if seed is None:
+        seed = 30 + EDGE_HEADS.index(H)
+    rng = np.random.default_rng(seed)
+    T, S, dqk, dv, W = 128, 128, 576, 512, 64
+    scale = 1.0 / math.sqrt(dqk)
+    q32 = rng.standard_normal(size=(T, H, dqk), dtype=np.float32)
+    kv = _bf16(rng, (S, dqk))
+    dO = _bf16(rng, (T, H, dv))
+    sink = torch.tensor([SATURATING_SINKS[(h + sink_cycle_offset) % 4] for h in range(H)],
+                        dtype=torch.float32)
+    idx = _causal_tiny_idxs(rng, T, W)
+    kvf = kv.double().numpy()
+    anti = []
+    for t in range(T):
+        if t % 4 == 0:
+            q32[t] *= np.float32(1e-3)
+        elif t % 4 == 1:
+            for _attempt in range(100):
+                rows = idx[t][idx[t] >= 0]
+                m = kvf[rows].sum(axis=0)
+                mhat = m / np.linalg.norm(m)
+                proj = kvf[rows] @ mhat
+                if proj.min() > 0:
+                    break
+                # redraw this row's index set
+                n = rows.size
+                idx[t] = -1
+                idx[t, :n] = rng.choice(t + 1, size=n, replace=False)
+            else:
+                continue
+            g = 100.0 / (scale * proj.min())
+            q32[t, :, :] = (-g * mhat).astype(np.float32)
+            anti.append(t)
+    q = torch.from_numpy(q32).to(torch.bfloat16)
+    return Problem(f"edge_sink_h{H}_o{sink_cycle_offset}", T, S, H, dqk, dv, W, scale,
+                   q, kv, dO, torch.from_numpy(idx), None, sink,
+                   meta=dict(seed=seed, anti_aligned_tokens=anti))
+
+
+def make_dsv4(T, H, d_qk, d_v, topk, seed, window=128, sink=True, compact=False,
+              scale=None, name=None):
+    """DeepSeek-V4-like: S_kv = T causal, window 128 + top-k distinct causal
+    indices from before the window, -1 padded; fp32 sink N(0,1).  ``compact``
+    packs the same index sets to the front with a length per token."""
+    rng = np.random.default_rng(seed)
+    q, kv, dO, s = _dense(rng, T, T, H, d_qk, d_v, sink)
+    idx = _window_topk_idxs(rng, T, window, topk)
+    length = None
+    if compact:
+        valid = idx >= 0
+        length = valid.sum(axis=1).astype(np.int32)
+        packed = np.full_like(idx, -1)
+        for t in range(T):
+            packed[t, : length[t]] = idx[t][valid[t]]
+        idx = packed
+        length = torch.from_numpy(length)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_qk)
+    return Problem(name or f"dsv4_T{T}_H{H}_d{d_qk}_k{topk}", T, T, H, d_qk, d_v,
+                   window + topk, scale, q, kv, dO, torch.from_numpy(idx), length, s,
+                   meta=dict(seed=seed, window=window, topk=topk, compact=compact))
+
+
+def make_problem(name: str, **kw) -> Problem:
+    return PROBLEMS[name](**kw)
+
+
+# The five workloads: tiny, the edge suite, and three DeepSeek-V4-like shapes.
+PROBLEMS = {
+    "tiny": make_tiny,
+    "edge_compact": make_edge_compact,
+    "edge_wide": make_edge_wide,
+    "edge_sink": make_edge_sink,
+    "dsv4_flash_h64": lambda **kw: make_dsv4(4096, 64, 512, 512, 512, seed=1,
+                                             name="dsv4_flash_h64_T4096", **kw),
+    "dsv4_flash_h128": lambda **kw: make_dsv4(4096, 128, 576, 512, 512, seed=2,
+                                              name="dsv4_flash_h128_T4096", **kw),
+    "dsv4_pro": lambda **kw: make_dsv4(16384, 128, 512, 512, 1024, seed=3,
+                                       name="dsv4_pro_h128_T16384", **kw),
+}
