@@ -1,0 +1,127 @@
+/*
+ * libsmla -- sparse top-k MLA attention (DeepSeek sparse attention) for AMD
+ * MI355X (gfx950).  C ABI.
+ *
+ * What the library computes.  For each query token t, H query heads share one
+ * latent KV row set (MQA): K = kv[:, :d_qk], V = kv[:, :d_v].  Token t attends
+ * only to the KV rows named by its valid top-k slots, plus an optional
+ * per-head sink logit that joins the softmax denominator and has no value row.
+ * Sources (page title, section):
+ *   [cuDNN-FE #785] "DSA backward SM90: fix three top-k and attention-sink
+ *                    boundary failures" -- Summary 1-3, Why 1-3, Not addressed
+ *   [cuDNN-FE #298] "DSA bwd SM100 fix dropped dKV gradients when topk width >
+ *                    total_S_kv"
+ *   [flash-attn #2882] "[CuTe, SM100] Support 1..128 Q heads in sparse MLA via
+ *                    in-kernel TMA padding" -- Agent Notes, Mechanism
+ *   [Automodel #3467] "Fix DeepSeek-V4 TileLang sparse-MLA backward
+ *                    compilation on Blackwell" -- review (validity mask)
+ *
+ * Slot validity.  Slot j of token t is valid iff
+ *   j < L_t   where L_t = clamp(topk_length[t], 0, W) if topk_length != NULL
+ *             (compact layout) and L_t = W otherwise (non-compact layout, -1
+ *             entries are padding) [cuDNN-FE #785 Why 2], and
+ *   0 <= topk_idxs[t][j] < S_kv   [Automodel #3467 review].
+ * The slot position is never compared with S_kv: in a non-compact row wider
+ * than S_kv, valid indices may sit at any column [cuDNN-FE #298].
+ *
+ * Conventions shared by every call.
+ *   - All tensors are dense, row-major, device memory, 16-byte aligned base
+ *     pointers.  bf16 tensors are passed as void* holding IEEE bfloat16.
+ *   - B > 1 batches are expressed by concatenating tokens and KV rows with
+ *     global row indices.
+ *   - Supported: d_qk in {512, 576}, d_v = 512, 1 <= H <= 128, W >= 1,
+ *     S_kv >= 1, T >= 0 (T = 0 is a no-op), scale finite.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     memory and never synchronises: work is enqueued on `stream` (a
+ *     hipStream_t; NULL means the null stream) and the call returns.
+ *   - Errors are reported by the return value before anything is enqueued;
+ *     SMLA_ERR_LAUNCH reports a failed kernel launch.  No global state is kept.
+ *   - Outputs are fully overwritten (a NaN-prefilled output comes back fully
+ *     written), including the rows of empty tokens.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_NULL = 1,        /* a required pointer is NULL                  */
+    SMLA_ERR_SHAPE = 2,       /* a size is negative or inconsistent          */
+    SMLA_ERR_UNSUPPORTED = 3, /* d_qk / d_v / H outside the supported range  */
+    SMLA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned       */
+    SMLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required     */
+    SMLA_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch     */
+} smla_status;
+
+/* Problem sizes.  T query tokens, S_kv KV rows, H heads, head widths d_qk and
+ * d_v (d_v <= d_qk; V is the first d_v columns of each kv row), W top-k slots
+ * per token, softmax scale (scores are scale * <q, k>). */
+typedef struct {
+    int32_t T, S_kv, H, d_qk, d_v, W;
+    float scale;
+} smla_dims;
+
+/* Forward [flash-attn #2882 Agent Notes; cuDNN-FE #785 Summary 2-3].
+ *   q          bf16 [T, H, d_qk]
+ *   kv         bf16 [S_kv, d_qk]
+ *   topk_idxs  int32 [T, W]
+ *   topk_length int32 [T] or NULL (NULL = non-compact layout)
+ *   attn_sink  fp32 [H] or NULL (NULL = no sink); +-inf and values beyond
+ *              the fp32 log2(e) rescale limit are handled (saturating sink)
+ *   o          bf16 [T, H, d_v]  out: softmax(valid scores + sink) @ V, the
+ *              sink column dropped; 0 for a token with no valid slot
+ *   lse        fp32 [T, H]       out: natural-log LSE of the valid scores,
+ *              WITHOUT the sink; -inf for a token with no valid slot
+ */
+smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
+                     const int32_t* topk_idxs, const int32_t* topk_length,
+                     const float* attn_sink, void* o, float* lse, void* stream);
+
+/* Backward preprocess [cuDNN-FE #785 Not addressed: Delta = O . dO, fp32
+ * reduction of the bf16-stored O].
+ *   o, dO      bf16 [T, H, d_v]
+ *   delta      fp32 [T, H]  out: sum_c o[t,h,c] * dO[t,h,c]
+ */
+smla_status smla_bwd_preprocess(const smla_dims* dims, const void* o, const void* dO,
+                                float* delta, void* stream);
+
+/* Bytes of device workspace smla_bwd needs for these sizes (0 if T == 0).
+ * Returns 0 for unsupported sizes as well; smla_bwd reports the error. */
+size_t smla_bwd_workspace_size(const smla_dims* dims);
+
+/* Backward of L = sum(dO * O) [cuDNN-FE #785 Summary 1-3, Why 1-3;
+ * cuDNN-FE #298].  Recomputes the probabilities from the forward's LSE and
+ * the sink, dP = dO V^T, dS = P (dP - Delta), and returns
+ *   dq         bf16 [T, H, d_qk] out: scale * dS K; 0 for a token with no
+ *              valid slot (that token's q, dO, lse and delta are not read)
+ *   dkv        fp32 [S_kv, d_qk] out: zeroed, then for every valid slot
+ *              dkv[idx, :d_qk] += scale * dS^T q and dkv[idx, :d_v] += P^T dO
+ *              (rows never named by a valid slot, e.g. row 0 for -1
+ *              sentinels, stay exactly 0)
+ *   d_sink     fp32 [H] out: -sum_t p_sink[t,h] * delta[t,h] with
+ *              p_sink = sigmoid(sink - lse); required iff attn_sink != NULL
+ * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16
+ * [T, H, d_v]; lse fp32 [T, H] from smla_fwd; delta fp32 [T, H] from
+ * smla_bwd_preprocess.  workspace: device memory of at least
+ * smla_bwd_workspace_size(dims) bytes, used by this call only.
+ */
+smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const void* dO,
+                     const float* lse, const float* delta, const int32_t* topk_idxs,
+                     const int32_t* topk_length, const float* attn_sink, void* dq,
+                     float* dkv, float* d_sink, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Static description of a status code. */
+const char* smla_status_string(smla_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,118 @@
+// C ABI of libsmla: argument validation and kernel dispatch.  Nothing here
+// allocates, frees or synchronises; every kernel goes to the caller's stream.
+#include "../../include/smla.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+smla_status check_dims(const smla_dims* d) {
+    if (d == nullptr) return SMLA_ERR_NULL;
+    if (d->T < 0 || d->S_kv < 1 || d->H < 1 || d->W < 1) return SMLA_ERR_SHAPE;
+    if ((d->d_qk != 512 && d->d_qk != 576) || d->d_v != 512 || d->H > 128)
+        return SMLA_ERR_UNSUPPORTED;
+    if (!(d->scale == d->scale) || d->scale == INFINITY || d->scale == -INFINITY)
+        return SMLA_ERR_SHAPE;
+    return SMLA_OK;
+}
+
+size_t round_up_blk(int W) { return ((size_t)W + smla::BLK - 1) / smla::BLK * smla::BLK; }
+
+}  // namespace
+
+extern "C" {
+
+const char* smla_status_string(smla_status s) {
+    switch (s) {
+        case SMLA_OK: return "ok";
+        case SMLA_ERR_NULL: return "a required pointer is NULL";
+        case SMLA_ERR_SHAPE: return "a size is negative or inconsistent";
+        case SMLA_ERR_UNSUPPORTED: return "unsupported d_qk / d_v / H";
+        case SMLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SMLA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+smla_status smla_fwd(const smla_dims* d, const void* q, const void* kv, const int32_t* topk_idxs,
+                     const int32_t* topk_length, const float* attn_sink, void* o, float* lse,
+                     void* stream) {
+    smla_status st = check_dims(d);
+    if (st != SMLA_OK) return st;
+    if (d->T == 0) return SMLA_OK;
+    if (!q || !kv || !topk_idxs || !o || !lse) return SMLA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return SMLA_ERR_ALIGN;
+    smla::FwdArgs a;
+    a.q = static_cast<const __bf16*>(q);
+    a.kv = static_cast<const __bf16*>(kv);
+    a.idx = topk_idxs;
+    a.len = topk_length;
+    a.sink = attn_sink;
+    a.o = static_cast<__bf16*>(o);
+    a.lse = lse;
+    a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
+    a.scale_log2 = d->scale * smla::LOG2E;
+    hipError_t e = smla::launch_fwd(d->d_qk, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+smla_status smla_bwd_preprocess(const smla_dims* d, const void* o, const void* dO, float* delta,
+                                void* stream) {
+    smla_status st = check_dims(d);
+    if (st != SMLA_OK) return st;
+    if (d->T == 0) return SMLA_OK;
+    if (!o || !dO || !delta) return SMLA_ERR_NULL;
+    if (!aligned16(o) || !aligned16(dO)) return SMLA_ERR_ALIGN;
+    hipError_t e = smla::launch_preprocess(static_cast<const __bf16*>(o),
+                                           static_cast<const __bf16*>(dO), delta, d->T * d->H,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+size_t smla_bwd_workspace_size(const smla_dims* d) {
+    if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
+    // P and scale*dS, bf16 [T, H, W rounded up to the 64-slot block]
+    return 2 * (size_t)d->T * d->H * round_up_blk(d->W) * sizeof(uint16_t);
+}
+
+smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                     const float* lse, const float* delta, const int32_t* topk_idxs,
+                     const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
+                     float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
+    smla_status st = check_dims(d);
+    if (st != SMLA_OK) return st;
+    if (!dkv) return SMLA_ERR_NULL;
+    if (attn_sink && !d_sink) return SMLA_ERR_NULL;
+    if (d->T > 0) {
+        if (!q || !kv || !dO || !lse || !delta || !topk_idxs || !dq) return SMLA_ERR_NULL;
+        if (!aligned16(q) || !aligned16(kv) || !aligned16(dO) || !aligned16(dq) || !aligned16(dkv))
+            return SMLA_ERR_ALIGN;
+        const size_t need = smla_bwd_workspace_size(d);
+        if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return SMLA_ERR_ALIGN;
+    }
+    smla::BwdArgs a;
+    a.q = static_cast<const __bf16*>(q);
+    a.kv = static_cast<const __bf16*>(kv);
+    a.dO = static_cast<const __bf16*>(dO);
+    a.lse = lse;
+    a.delta = delta;
+    a.idx = topk_idxs;
+    a.len = topk_length;
+    a.sink = attn_sink;
+    a.dq = static_cast<__bf16*>(dq);
+    a.dkv = dkv;
+    a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
+    a.Wp = (int)round_up_blk(d->W);
+    a.ws_p = static_cast<__bf16*>(workspace);
+    a.ws_ds = a.ws_p + (size_t)d->T * d->H * a.Wp;
+    a.scale = d->scale;
+    a.scale_log2 = d->scale * smla::LOG2E;
+    hipError_t e = smla::launch_bwd(d->d_qk, a, d_sink, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device-side building blocks shared by the sparse MLA kernels (gfx950).
+//
+// Operand layouts of the bf16 MFMA used throughout, v_mfma_f32_16x16x32_bf16
+// (checked on the hardware): with lane l, g = l / 16 and n = l % 16,
+//   A (16 x 32): lane holds A[n][8g .. 8g+7]
+//   B (32 x 16): lane holds B[8g .. 8g+7][n]
+//   C (16 x 16): lane holds C[4g .. 4g+3][n]
+// The contraction index is always the in-lane one.  ds_read_b64_tr_b16 reads
+// a 4 x 16 block of 16-bit values spread over a 16-lane group (lanes 4e..4e+3
+// name row e, four columns each) and returns to lane i of the group the column
+// i of that block (rows 0..3), i.e. a transposed operand straight from LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+
+constexpr int BLK = 64;           // top-k slots per block
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 zero8() {
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 lds8(const __bf16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// Transposed 4-element read from LDS (see the file comment).
+__device__ __forceinline__ bf16x4 lds_tr4(const __bf16* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_bf16*)p));
+}
+
+__device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
+    return bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+
+__device__ __forceinline__ bf16x8 cvt8(f32x4 lo, f32x4 hi) {
+    return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                  (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+}
+
+__device__ __forceinline__ void st4(__bf16* p, bf16x4 v) {
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor_max(float v, int m) {
+    return fmaxf(v, __shfl_xor(v, m, 64));
+}
+
+// Number of valid-candidate slots of token t: the compact length clamped to
+// [0, W], or W for the non-compact layout.
+__device__ __forceinline__ int row_length(const int32_t* len, int t, int W) {
+    if (len == nullptr) return W;
+    int L = len[t];
+    return L < 0 ? 0 : (L > W ? W : L);
+}
+
+// KV row of slot j, or -1 when the slot is not valid.
+__device__ __forceinline__ int slot_row(const int32_t* idx, int t, int W, int L, int S_kv, int j) {
+    if (j >= L) return -1;
+    int v = idx[(size_t)t * W + j];
+    return (v >= 0 && v < S_kv) ? v : -1;
+}
+
+// Finite-max-guarded logaddexp: ln(e^a + e^b); an infinite maximum is returned
+// as is, so no inf - inf is formed.
+__device__ __forceinline__ float glae(float a, float b) {
+    float m = fmaxf(a, b);
+    if (m == INFINITY || m == -INFINITY) return m;
+    return m + logf(expf(a - m) + expf(b - m));
+}
+
+// sigma(x) = 1 / (1 + e^-x), saturating cleanly at both ends.
+__device__ __forceinline__ float sigmoid(float x) {
+    return 1.0f / (1.0f + expf(-x));
+}
+
+}  // namespace smla

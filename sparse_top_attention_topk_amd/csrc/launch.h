@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+struct FwdArgs {
+    const __bf16* q;
+    const __bf16* kv;
+    const int32_t* idx;
+    const int32_t* len;
+    const float* sink;
+    __bf16* o;
+    float* lse;
+    int T, S_kv, H, W;
+    float scale_log2;   // scale * log2(e)
+};
+
+struct BwdArgs {
+    const __bf16* q;
+    const __bf16* kv;
+    const __bf16* dO;
+    const float* lse;
+    const float* delta;
+    const int32_t* idx;
+    const int32_t* len;
+    const float* sink;
+    __bf16* dq;
+    float* dkv;
+    __bf16* ws_p;     // [T, H, Wp] bf16: P
+    __bf16* ws_ds;    // [T, H, Wp] bf16: scale * dS
+    int T, S_kv, H, W, Wp;
+    float scale, scale_log2;
+};
+
+hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,
+                             hipStream_t stream);
+hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream);
+
+}  // namespace smla

@@ -171,6 +171,20 @@ def make_edge_wide(H, seed=None, T=128, S=256, W=1024):
                    q, kv, dO, torch.from_numpy(idx), None, s, meta=dict(seed=seed))
 
 
+def make_edge_width118(H, seed=40, T=64, S=128):
+    """Non-compact width 118 = 100 valid indices at random positions + 18 -1
+    entries per row (a 54-slot partial last block, [cuDNN-FE #785] review)."""
+    rng = np.random.default_rng(seed)
+    W, dqk, dv = 118, 576, 512
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        pos = rng.choice(W, size=100, replace=False)
+        idx[t, pos] = rng.choice(S, size=100, replace=False)
+    return Problem(f"edge_w118_h{H}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), None, s, meta=dict(seed=seed))
+
+
 SATURATING_SINKS = (3.0e38, -3.0e38, float("inf"), float("-inf"))
 
 

@@ -1,0 +1,90 @@
+"""The C-ABI library: it loads, exports every symbol include/smla.h declares,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_top_attention_topk_amd import build_lib
+    if not os.path.exists(build_lib.LIB):
+        build_lib.build()
+    from sparse_top_attention_topk_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:smla_status|size_t|const char\*)\s+(smla_\w+)\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd",
+                                           "smla_bwd_workspace_size", "smla_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (smla_\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib.LIB, name)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.LIB.smla_status_string(code)
+    assert lib.LIB.smla_status_string(0) == b"ok"
+
+
+def _dims(lib, **kw):
+    base = dict(T=4, S_kv=8, H=2, d_qk=576, d_v=512, W=4, scale=0.1)
+    base.update(kw)
+    return lib.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_qk=128), 3), (dict(d_v=256), 3), (dict(H=129), 3), (dict(H=0), 2),
+    (dict(W=0), 2), (dict(S_kv=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2),
+])
+def test_fwd_rejects_bad_dims(lib, kw, code):
+    d = _dims(lib, **kw)
+    st = lib.LIB.smla_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None)
+    assert st == code
+
+
+def test_null_pointers_and_alignment(lib):
+    d = _dims(lib)
+    assert lib.LIB.smla_fwd(None, None, None, None, None, None, None, None, None) == 1
+    assert lib.LIB.smla_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None) == 1
+    p = ctypes.c_void_p(0x1000)
+    q = ctypes.c_void_p(0x1008)       # not 16-byte aligned
+    assert lib.LIB.smla_fwd(ctypes.byref(d), q, p, p, None, None, p, p, None) == 4
+    assert lib.LIB.smla_bwd_preprocess(ctypes.byref(d), None, p, p, None) == 1
+
+
+def test_empty_problem_is_a_no_op(lib):
+    d = _dims(lib, T=0)
+    assert lib.LIB.smla_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
+    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == 0
+
+
+def test_workspace_size_and_check(lib):
+    d = _dims(lib, T=3, H=5, W=70)
+    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == 2 * 3 * 5 * 128 * 2
+    p = ctypes.c_void_p(0x1000)
+    st = lib.LIB.smla_bwd(ctypes.byref(d), p, p, p, p, p, p, None, None, p, p, None, p,
+                          ctypes.c_size_t(10), None)
+    assert st == 5
+    # a sink without a d_sink output
+    st = lib.LIB.smla_bwd(ctypes.byref(d), p, p, p, p, p, p, None, p, p, p, None, p,
+                          ctypes.c_size_t(1 << 20), None)
+    assert st == 1

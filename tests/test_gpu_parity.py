@@ -1,0 +1,142 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small problems are compared element by element on every output.  The three
+DeepSeek-V4-like workloads run at their full size in the same launch
+configuration as bench.py and are compared on sampled tokens (O, LSE, dQ) and
+sampled KV rows (dKV, computed exactly from every token that names the row),
+plus identities that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity import (compare_full, compare_exact_delta, run_gpu, run_oracle, say, check_tensor,
+                    check_lse, referenced_rows, tokens_referencing)
+from sparse_top_attention_topk_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _run_and_compare(p, label):
+    say(f"[gpu] case {label}: T={p.T} S_kv={p.S_kv} H={p.H} d_qk={p.d_qk} W={p.W} "
+        f"compact={p.topk_length is not None} sink={p.attn_sink is not None}")
+    gpu = run_gpu(p, DEV)
+    ref = run_oracle(p)
+    errors = compare_full(gpu, ref)
+    compare_exact_delta(gpu, run_oracle(p, delta_from="fp64"), errors)
+    assert not errors, f"{label}: " + "; ".join(errors)
+    return gpu, ref
+
+
+@pytest.mark.parametrize("variant", ["sink", "nosink", "compact"])
+def test_tiny(variant):
+    p = wl.make_tiny(seed=0, sink=variant != "nosink", compact=variant == "compact")
+    _run_and_compare(p, f"tiny-{variant}")
+
+
+@pytest.mark.parametrize("H", wl.EDGE_HEADS)
+def test_edge_compact(H):
+    p = wl.make_edge_compact(H)
+    gpu, ref = _run_and_compare(p, f"edge-compact-h{H}")
+    ln = p.topk_length.numpy()
+    empty = np.nonzero(ln == 0)[0]
+    assert empty.size > 0
+    assert np.all(gpu["o"][empty] == 0) and np.all(np.isneginf(gpu["lse"][empty]))
+    assert np.all(gpu["dq"][empty] == 0)
+
+
+@pytest.mark.parametrize("H", wl.EDGE_HEADS)
+def test_edge_wide_noncompact(H):
+    p = wl.make_edge_wide(H)
+    gpu, ref = _run_and_compare(p, f"edge-wide-h{H}")
+    # rows named only at columns >= S_kv still receive dKV
+    idx = p.topk_idxs.numpy()
+    late = np.unique(idx[:, p.S_kv:][idx[:, p.S_kv:] >= 0])
+    assert late.size > 0 and np.all(np.any(gpu["dkv"][late] != 0, axis=1))
+    # rows never named (row 0 included when unnamed) are exactly 0
+    unnamed = ~referenced_rows(p)
+    assert np.all(gpu["dkv"][unnamed] == 0)
+
+
+@pytest.mark.parametrize("H", wl.EDGE_HEADS)
+def test_edge_saturating_sinks(H):
+    offsets = range(4) if H == 1 else (0,)
+    for off in offsets:
+        p = wl.make_edge_sink(H, sink_cycle_offset=off)
+        gpu, ref = _run_and_compare(p, f"edge-sink-h{H}-o{off}")
+        anti = np.array(p.meta["anti_aligned_tokens"])
+        assert ref["lse"][anti].max() < -80        # the case exercises the overflow
+        s = p.attn_sink.numpy()
+        pos = s > 2.36e38                            # +3e38 and +inf heads take all mass
+        assert np.all(gpu["o"][:, pos] == 0) and np.all(gpu["dq"][:, pos] == 0)
+
+
+@pytest.mark.parametrize("H", (24, 128))
+def test_width_118_tail(H):
+    """Non-compact width 118 = 100 valid + 18 padding: a partial last block."""
+    _run_and_compare(wl.make_edge_width118(H), f"width-118-h{H}")
+
+
+def test_nan_prefilled_outputs_fully_written_and_deterministic():
+    p = wl.make_edge_compact(64)
+    a = run_gpu(p, DEV, nan_prefill=True)
+    b = run_gpu(p, DEV, nan_prefill=False)
+    for k in ("o", "lse", "dq", "d_sink"):
+        assert np.array_equal(a[k], b[k], equal_nan=False), k
+    assert np.all(np.isfinite(a["o"])) and np.all(np.isfinite(a["dq"]))
+
+
+def test_repeated_empty_and_mixed_rows():
+    """Repeated launches of the empty-row path (all-empty and mixed rows),
+    compared bit for bit across launches."""
+    p = wl.make_edge_compact(128)
+    p_empty = wl.make_edge_compact(128)
+    p_empty.topk_length = torch.zeros_like(p_empty.topk_length)
+    ref_m = run_gpu(p, DEV)
+    ref_e = run_gpu(p_empty, DEV)
+    assert np.all(ref_e["o"] == 0) and np.all(ref_e["dq"] == 0) and np.all(ref_e["dkv"] == 0)
+    for _ in range(20):
+        for pp, rr in ((p, ref_m), (p_empty, ref_e)):
+            g = run_gpu(pp, DEV)
+            assert np.array_equal(g["o"], rr["o"]) and np.array_equal(g["dq"], rr["dq"])
+            np.testing.assert_allclose(g["dkv"], rr["dkv"], rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, as bench.py runs them
+# ---------------------------------------------------------------------------
+FULL = ["dsv4_flash_h64", "dsv4_flash_h128", "dsv4_pro"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    p = wl.make_problem(name)
+    say(f"[gpu] full-size {name}: T={p.T} H={p.H} d_qk={p.d_qk} W={p.W}")
+    gpu = run_gpu(p, DEV, nan_prefill=False)
+    T = p.T
+    errors = []
+    for k in ("o", "dq", "dkv"):
+        if not np.all(np.isfinite(gpu[k])):
+            errors.append(f"{k}: non-finite entries")
+    # sampled tokens: first, last, and spread over the range
+    toks = np.unique(np.concatenate([[0, 1, 127, 128, 640, T // 2, T - 2, T - 1],
+                                     np.random.default_rng(7).integers(0, T, 8)]))
+    ref = run_oracle(p, tokens=toks)
+    check_tensor("o[sampled]", gpu["o"][toks], ref["o"], errors)
+    check_lse(gpu["lse"][toks], ref["lse"], errors)
+    check_tensor("dq[sampled]", gpu["dq"][toks], ref["dq"], errors)
+    # sampled KV rows: exact dKV from every token that names them
+    rows = np.array([T - 1, T - 64, T // 2])
+    toks_r = tokens_referencing(p, rows)
+    say(f"[gpu] full-size {name}: dKV rows {rows.tolist()} named by {toks_r.size} tokens")
+    ref_r = run_oracle(p, tokens=toks_r)
+    check_tensor("dkv[sampled rows]", gpu["dkv"][rows], ref_r["dkv"][rows], errors)
+    # structural: rows never named are exactly zero, named rows are nonzero
+    named = referenced_rows(p)
+    if np.any(gpu["dkv"][~named] != 0):
+        errors.append("dkv: unnamed rows are not zero")
+    if not np.all(np.any(gpu["dkv"][named] != 0, axis=1)):
+        errors.append("dkv: a named row received nothing")
+    assert not errors, f"{name}: " + "; ".join(errors)
