@@ -1,0 +1,206 @@
+"""Benchmark: sparse MLA forward + backward on one MI355X.
+
+One step = smla_fwd + smla_bwd_preprocess + smla_bwd over one batch of the
+synthetic workload (inputs already resident in HBM).  Default workload:
+DeepSeek-V4-like H=128, T = S_kv = 4096 causal, d_qk = 576 (512 latent + 64
+rope), d_v = 512, window 128 + top-k 512 slots per token, -1 padded,
+non-compact, fp32 sink.
+
+FLOP convention of the pages ([flash-attn #2882] Performance): forward
+2 * H * K * (d_qk + d_v) per token with K the valid gathered slots, backward
+2.5x the forward.  Gathered bytes (the pages' TB/s model): gathered KV rows
+(K * d_qk * 2 bytes per token) + Q read + O write.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA fwd+bwd TFLOPS & gather TB/s, H=128 T=4096 topk=512, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0           # HBM3E, MI355X
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv4_flash_h128")
+    ap.add_argument("--cpu-tokens", type=int, default=384,
+                    help="tokens of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+              "(no collectives, no sharding).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from sparse_top_attention_topk_amd import _lib, workloads as wl
+
+    dev = torch.device("cuda:0")
+    p = wl.make_problem(args.workload)
+    n_valid = p.valid_count()
+    fwd_flop = 2.0 * p.H * (p.d_qk + p.d_v) * n_valid
+    bwd_flop = 2.5 * fwd_flop
+    gathered = n_valid * p.d_qk * 2 + p.T * p.H * (p.d_qk + p.d_v) * 2
+
+    q, kv, dO = p.q.to(dev), p.kv.to(dev), p.dO.to(dev)
+    idx = p.topk_idxs.to(dev)
+    length = None if p.topk_length is None else p.topk_length.to(dev)
+    sink = None if p.attn_sink is None else p.attn_sink.to(dev)
+    o = torch.empty((p.T, p.H, p.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((p.T, p.H), dtype=torch.float32, device=dev)
+    delta = torch.empty((p.T, p.H), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q)
+    dkv = torch.empty((p.S_kv, p.d_qk), dtype=torch.float32, device=dev)
+    d_sink = torch.empty((p.H,), dtype=torch.float32, device=dev) if sink is not None else None
+    ws_bytes = _lib.smla_bwd_workspace_size(p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        _lib.smla_fwd(q, kv, idx, length, sink, p.scale, o=o, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        _lib.smla_bwd_preprocess(o, dO, delta=delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        _lib.smla_bwd(q, kv, dO, lse, delta, idx, length, sink, p.scale, dq=dq, dkv=dkv,
+                      d_sink=d_sink, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pre_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    total_flop = fwd_flop + bwd_flop
+    value = total_flop / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the forward kernel is the only kernel of smla_fwd, so the
+    # events around smla_fwd bracket it exactly
+    fwd_s = float(np.mean(fwd_ms)) * 1e-3
+    achieved_gbs = gathered / fwd_s / 1e9
+    roofline = {
+        "kernel": "fwd_kernel<576,2> (smla_fwd)",
+        "bound": "hbm",
+        "achieved": round(achieved_gbs, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": int(gathered),
+        "mfma_tflops": round(fwd_flop / fwd_s / 1e12, 1),
+        "mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(p, args.cpu_tokens)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": p.name,
+            "T": p.T, "S_kv": p.S_kv, "H": p.H, "d_qk": p.d_qk, "d_v": p.d_v, "W": p.W,
+            "window": p.meta.get("window"), "topk": p.meta.get("topk"),
+            "layout": "compact" if p.topk_length is not None else "non-compact",
+            "sink": p.attn_sink is not None, "valid_slots": n_valid,
+        },
+        "detail": {
+            "fwd_us": round(float(np.mean(fwd_ms)) * 1e3, 1),
+            "bwd_preprocess_us": round(float(np.mean(pre_ms)) * 1e3, 1),
+            "bwd_us": round(float(np.mean(bwd_ms)) * 1e3, 1),
+            "step_us_events": round(float(np.mean(step_ms)) * 1e3, 1),
+            "fwd_tflops": round(fwd_flop / fwd_s / 1e12, 1),
+            "bwd_tflops": round(bwd_flop / (float(np.mean(pre_ms + bwd_ms)) * 1e-3) / 1e12, 1),
+            "fwd_gathered_tbs": round(gathered / fwd_s / 1e12, 3),
+            "fwd_flop": fwd_flop, "bwd_flop": bwd_flop, "gathered_bytes_fwd": gathered,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(p, n_tokens):
+    """The fp64 oracle, as it stands, on the last n_tokens tokens of the same
+    workload (full-width rows), forward + backward, on this host's cores."""
+    import oracle
+    toks = np.arange(max(0, p.T - n_tokens), p.T)
+    tk = torch.from_numpy(toks)
+    x = dict(q=p.q[tk].double().numpy(), kv=p.kv.double().numpy(), dO=p.dO[tk].double().numpy(),
+             idx=p.topk_idxs[tk].numpy(),
+             length=None if p.topk_length is None else p.topk_length[tk].numpy(),
+             sink=None if p.attn_sink is None else p.attn_sink.double().numpy())
+    idx = x["idx"]
+    ok = (idx >= 0) & (idx < p.S_kv)
+    if x["length"] is not None:
+        ok &= np.arange(p.W)[None, :] < np.clip(x["length"], 0, p.W)[:, None]
+    n_valid = int(ok.sum())
+    flop = 3.5 * 2.0 * p.H * (p.d_qk + p.d_v) * n_valid
+    t0 = time.perf_counter()
+    oracle.oracle_fwd(x["q"], x["kv"], idx, x["length"], x["sink"], p.scale, p.d_v)
+    oracle.oracle_bwd(x["q"], x["kv"], x["dO"], idx, x["length"], x["sink"], p.scale, p.d_v)
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {
+        "value": round(flop / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"fwd+bwd of the last {len(toks)} tokens ({n_valid} valid slots) of {p.name}, "
+                  f"fp64 NumPy, {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

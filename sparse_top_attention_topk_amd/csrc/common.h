@@ -23,6 +23,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BLK = 64;           // top-k slots per block
 constexpr float LOG2E = 1.4426950408889634f;
@@ -70,6 +71,10 @@ __device__ __forceinline__ void st4(__bf16* p, bf16x4 v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Wait until every vector-memory operation of this wave has completed
+// (including direct global->LDS loads).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70 & ~0xC000); }
 
 __device__ __forceinline__ float xor_max(float v, int m) {
     return fmaxf(v, __shfl_xor(v, m, 64));

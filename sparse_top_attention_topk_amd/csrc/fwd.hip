@@ -3,172 +3,311 @@
 // Method ([flash-attn #2882] Agent Notes; [cuDNN-FE #785] Summary 2-3): for
 // each token, the H query heads share the token's gathered KV rows.  Per block
 // of 64 top-k slots the workgroup
-//   1. resolves slot -> KV row (invalid slots -> -1) and gathers the rows into
-//      an LDS tile (zeros for invalid slots);
-//   2. computes S^T = K Q^T with bf16 MFMA (slots x heads, fp32 accumulate);
-//      each wave owns NT x 16 heads and holds their Q in registers, padded
+//   1. resolves slot -> KV row (invalid slots -> -1) two blocks ahead;
+//   2. gathers the rows of the NEXT block into the other of two LDS tiles with
+//      asynchronous direct global->LDS 16-byte loads, so that the gather of
+//      block b+1 is in flight while block b is computed (the pages find the
+//      gather latency to be the bottleneck, [flash-attn #2882] Performance);
+//   3. computes S^T = K Q^T with bf16 MFMA (slots x heads, fp32 accumulate);
+//      each wave owns NT x 16 heads and keeps their Q in registers; padded
 //      heads (h >= H) are zero rows, so any H in 1..128 runs without padded
-//      copies in memory;
-//   3. masks invalid slots to -inf before any exponential, then runs an
-//      online softmax in the log2 domain (running max and sum per head);
-//   4. accumulates O^T += V^T P^T with V^T read transposed from the same tile.
-// The epilogue folds the sink: O = acc / l * sigmoid(lse - sink), where the
-// sigmoid is the sink-free share of the mass ([cuDNN-FE #785] Why 3), and
-// writes the sink-free natural-log LSE.  Empty rows write O = 0, LSE = -inf.
+//      copies in memory ([flash-attn #2882] Mechanism);
+//   4. masks invalid slots to -inf before any exponential ([cuDNN-FE #785]
+//      Summary 2) and exponentiates in the log2 domain against a per-head
+//      reference max fixed at the head's first valid block (no rescaling of
+//      O inside the loop; see REF_SLACK);
+//   5. accumulates O^T += V^T P^T, V^T read transposed from the same tile.
+// The epilogue folds the sink, O = acc / l * sigmoid(lse - sink), the
+// sink-free share of the softmax mass written without forming inf - inf
+// ([cuDNN-FE #785] Why 3), stages O through LDS for coalesced stores, and
+// writes the sink-free natural-log LSE.  Empty rows give O = 0, LSE = -inf.
 #include "kv_tile.h"
 #include "launch.h"
 
 namespace smla {
 
+// A head's reference max is fixed at its first valid block and O is never
+// rescaled inside the loop: P = 2^(s - m_ref) and the fp32 accumulators share
+// fp32's exponent range, so scores up to REF_SLACK above the reference are
+// exact up to rounding.  A token whose scores rise further than that is rerun
+// with the exact max as reference (a second pass; rare).
+constexpr float REF_SLACK = 64.0f;   // log2 units
 
-template <int DQK, int NT>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdArgs a) {
-    constexpr int DV = 512;
-    constexpr int KS = DQK / 32;      // k-steps of S^T
-    constexpr int MC = DV / 16;       // 16-column tiles of O^T
-    using Tile = KvTile<DQK>;
-    __shared__ __attribute__((aligned(16))) __bf16 s_tile[Tile::ELEMS];
-    __shared__ int s_row[BLK];
+template <int DQK, int NW, int NT>
+struct FwdCfg {
+    static constexpr int DV = 512;
+    static constexpr int KS = DQK / 32;      // k-steps of S^T
+    static constexpr int MC = DV / 16;       // 16-column tiles of O^T
+    static constexpr int HT = NW * NT * 16;  // heads per workgroup
+    using Tile = KvTileSwz<DQK>;
+};
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One 64-slot block, as two halves of 32 slots: S^T for the half, mask,
+// P = 2^(s - m_ref), then O^T += V^T P^T over the half.
+template <int DQK, int NW, int NT>
+__device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
+                                          const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
+                                          const bf16x8 (&qop)[NT][DQK / 32],
+                                          f32x4 (&oacc)[512 / 16][NT], float (&m_ref)[NT],
+                                          float (&rmax)[NT], float (&l_run)[NT],
+                                          float (&l_rnd)[NT], int lane) {
+    using C = FwdCfg<DQK, NW, NT>;
+    using Tile = typename C::Tile;
+    const int g = lane >> 4;
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        // S^T for slots 32 half .. +31; K operands one k-step ahead
+        f32x4 sacc[2][NT];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = zero4();
+        bf16x8 kop[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) kop[0][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, 0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < C::KS) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    kop[cur ^ 1][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, ks + 1);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[m][nt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // mask invalid slots before the exponential; log2-domain scores
+        float hmax[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) hmax[nt] = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const float sv = ok ? sacc[m][nt][i] * a.scale_log2 : -INFINITY;
+                    sacc[m][nt][i] = sv;
+                    hmax[nt] = fmaxf(hmax[nt], sv);
+                }
+            }
+        }
+        // heads without a reference yet take this half's max (all lanes of a
+        // head agree after the reduction)
+        bool unset = false;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            rmax[nt] = fmaxf(rmax[nt], hmax[nt]);
+            unset |= m_ref[nt] == -INFINITY;
+        }
+        if (__builtin_amdgcn_ballot_w64(unset) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float hm = xor_max(xor_max(hmax[nt], 16), 32);
+                if (m_ref[nt] == -INFINITY) m_ref[nt] = hm;
+            }
+        }
+        bf16x8 pop[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float m_use = (m_ref[nt] == -INFINITY) ? 0.f : m_ref[nt];
+            float psum = 0.f;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = fast_exp2(sacc[m][nt][i] - m_use);
+                    sacc[m][nt][i] = p;
+                    psum += p;
+                }
+            l_run[nt] += psum;
+            pop[nt] = cvt8(sacc[0][nt], sacc[1][nt]);
+            // the sum of the bf16 weights the MFMA actually uses: O is
+            // normalised by it, so O stays an exact convex combination of the
+            // gathered V rows (a near one-hot row reproduces its V row)
+            float rsum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) rsum += (float)pop[nt][j];
+            l_rnd[nt] += rsum;
+        }
+
+        // O^T += V^T P^T over slots 32 half .. +31, V^T one column tile ahead
+        bf16x8 vop[2];
+        vop[0] = Tile::slot_op(tile, TL, 32 * half, 0);
+#pragma unroll
+        for (int mc = 0; mc < C::MC; ++mc) {
+            const int cur = mc & 1;
+            if (mc + 1 < C::MC) vop[cur ^ 1] = Tile::slot_op(tile, TL, 32 * half, mc + 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = mfma16(vop[cur], pop[nt], oacc[mc][nt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// topk_idxs[t][j] for any j (clamped into the row so the read is in bounds);
+// its validity is decided later by valid_row, where the value is consumed.
+__device__ __forceinline__ int raw_index(const FwdArgs& a, int t, int j) {
+    return a.idx[(size_t)t * a.W + (j < a.W ? j : a.W - 1)];
+}
+
+__device__ __forceinline__ int valid_row(int v, int j, int L, int S_kv) {
+    return (j < L && v >= 0 && v < S_kv) ? v : -1;
+}
+
+template <int DQK, int NW, int NT>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
+    using C = FwdCfg<DQK, NW, NT>;
+    using Tile = typename C::Tile;
+    constexpr int NTH = NW * 64;
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
+    __shared__ int s_rows[3][BLK];
+    __shared__ int s_rerun;
+    static_assert(64 * C::DV <= Tile::ELEMS && C::HT <= 128, "O staging must fit in the tiles");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar
     const int g = lane >> 4, n = lane & 15;
     const int t = a.T - 1 - (int)blockIdx.x;          // longest rows first
-    const int h_wave = (int)blockIdx.y * (4 * NT * 16) + wave * NT * 16;
+    const int h_wg = (int)blockIdx.y * C::HT;
+    const int h_wave = h_wg + wave * NT * 16;
     const bool active = h_wave < a.H;                 // wave-uniform
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
 
+    if (tid == 0) s_rerun = 0;
+
     // Q as the B operand of S^T = K Q^T: lane (g, n) holds q[t, head, 32ks+8g..+7]
-    bf16x8 qop[NT][KS];
+    bf16x8 qop[NT][C::KS];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int head = h_wave + nt * 16 + n;
-        const __bf16* qp = a.q + ((size_t)t * a.H + (head < a.H ? head : 0)) * DQK + 8 * g;
+        const bool hv = head < a.H && nblk > 0;
+        const __bf16* qp = a.q + ((size_t)t * a.H + (hv ? head : 0)) * DQK + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qop[nt][ks] = (head < a.H && nblk > 0) ? ld8(qp + 32 * ks) : zero8();
+        for (int ks = 0; ks < C::KS; ++ks) qop[nt][ks] = hv ? ld8(qp + 32 * ks) : zero8();
     }
+    const typename Tile::Lane TL = Tile::lane_bases(lane);
+    f32x4 oacc[C::MC][NT];
+    float m_ref[NT], rmax[NT], l_run[NT], l_rnd[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) m_ref[nt] = -INFINITY;
 
-    f32x4 oacc[MC][NT];
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc)
+        for (int mc = 0; mc < C::MC; ++mc)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = zero4();
-    float m_run[NT], l_run[NT];
+            for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = zero4();
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
+        for (int nt = 0; nt < NT; ++nt) { rmax[nt] = -INFINITY; l_run[nt] = 0.f; l_rnd[nt] = 0.f; }
 
-    for (int b = 0; b < nblk; ++b) {
+        if (tid < BLK) {
+            s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
+            s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
+        }
         __syncthreads();
-        Tile::load_rows(s_row, a.idx, t, a.W, L, a.S_kv, b);
-        __syncthreads();
-        Tile::gather(s_tile, s_row, a.kv);
-        __syncthreads();
-        if (!active) continue;
+        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], a.kv, wave, lane);
 
-        // S^T tiles: 4 row tiles of 16 slots x NT column tiles of 16 heads
-        f32x4 sacc[4][NT];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 kop = Tile::row_op(s_tile, mt * 16, ks * 32, lane);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) sacc[mt][nt] = mfma16(kop, qop[nt][ks], sacc[mt][nt]);
-            }
+        // Two blocks per iteration so that each tile is a distinct LDS object.
+        // Per block: wait for this block's tile, start the next block's
+        // gather, fetch the slot rows two blocks ahead (issued before the
+        // gather, stored after the math), compute.
+        for (int b = 0; b < nblk; b += 2) {
+            // ---- block b in tile 0
+            wait_vmem();
+            __syncthreads();
+            int ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
+            __builtin_amdgcn_sched_barrier(0);
+            if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane);
+            if (active) fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
+            if (b + 2 < nblk && tid < BLK)
+                s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
+            if (b + 1 >= nblk) break;
+            // ---- block b+1 in tile 1
+            wait_vmem();
+            __syncthreads();
+            ahead = tid < BLK ? raw_index(a, t, (b + 3) * BLK + tid) : 0;
+            __builtin_amdgcn_sched_barrier(0);
+            if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane);
+            if (active) fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
+            if (b + 3 < nblk && tid < BLK)
+                s_rows[(b + 3) % 3][tid] = valid_row(ahead, (b + 3) * BLK + tid, L, a.S_kv);
         }
 
-        // mask invalid slots before the exponential; log2-domain scores
-        float blk_max[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) blk_max[nt] = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = s_row[mt * 16 + 4 * g + i] >= 0;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const float s = ok ? sacc[mt][nt][i] * a.scale_log2 : -INFINITY;
-                    sacc[mt][nt][i] = s;
-                    blk_max[nt] = fmaxf(blk_max[nt], s);
-                }
-            }
-        }
-        bf16x8 pop[2][NT];
+        // did any head's scores rise more than REF_SLACK above its reference?
+        bool far = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            float mb = xor_max(xor_max(blk_max[nt], 16), 32);
-            const float m_new = fmaxf(m_run[nt], mb);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[nt] - m_use);
-            float psum = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(sacc[mt][nt][i] - m_use);
-                    sacc[mt][nt][i] = p;
-                    psum += p;
-                }
-            l_run[nt] = l_run[nt] * alpha + psum;
-            m_run[nt] = m_new;
-#pragma unroll
-            for (int mc = 0; mc < MC; ++mc) oacc[mc][nt] *= alpha;
-            pop[0][nt] = cvt8(sacc[0][nt], sacc[1][nt]);
-            pop[1][nt] = cvt8(sacc[2][nt], sacc[3][nt]);
+            rmax[nt] = xor_max(xor_max(rmax[nt], 16), 32);
+            far |= rmax[nt] > m_ref[nt] + REF_SLACK;
         }
-
-        // O^T += V^T P^T
+        if (pass == 0 && active && __builtin_amdgcn_ballot_w64(far) != 0 && lane == 0) s_rerun = 1;
+        __syncthreads();                // tiles and s_rows are free; s_rerun is final
+        if (pass == 1 || s_rerun == 0) break;
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 vop = Tile::slot_op(s_tile, kk * 32, mc * 16, lane);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = mfma16(vop, pop[kk][nt], oacc[mc][nt]);
-            }
-        }
+        for (int nt = 0; nt < NT; ++nt) m_ref[nt] = rmax[nt];    // exact max: P <= 1
+        __syncthreads();
     }
 
-    if (!active) return;
+    // epilogue: normalise, fold the sink, stage O^T through LDS as O rows
+    float lse_v[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int head = h_wave + nt * 16 + n;
-        float l = l_run[nt];
+        float l = l_run[nt], lr = l_rnd[nt];
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
+        lr += __shfl_xor(lr, 16, 64);
+        lr += __shfl_xor(lr, 32, 64);
         const bool nonempty = l > 0.f;
-        const float lse = nonempty ? (m_run[nt] + fast_log2(l)) * LN2 : -INFINITY;
-        float f = nonempty ? 1.0f / l : 0.f;
-        if (a.sink != nullptr && nonempty && head < a.H) f *= sigmoid(lse - a.sink[head]);
-        if (head < a.H) {
-            __bf16* op = a.o + ((size_t)t * a.H + head) * DV + 4 * g;
+        lse_v[nt] = nonempty ? (m_ref[nt] + fast_log2(l)) * LN2 : -INFINITY;
+        float f = (nonempty && lr > 0.f) ? 1.0f / lr : 0.f;
+        if (a.sink != nullptr && nonempty && head < a.H) f *= sigmoid(lse_v[nt] - a.sink[head]);
+        // staging row hr holds O[head] with 16-byte chunk c at c ^ (hr % 16)
+        const int hr = wave * NT * 16 + nt * 16 + n;
+        __bf16* sp = hr < 64 ? s_tile0 + hr * C::DV : s_tile1 + (hr - 64) * C::DV;
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) {
-                const f32x4 v = oacc[mc][nt] * f;
-                st4(op + mc * 16, cvt4(v[0], v[1], v[2], v[3]));
-            }
-            if (g == 0) a.lse[(size_t)t * a.H + head] = lse;
+        for (int mc = 0; mc < C::MC; ++mc) {
+            const f32x4 v = oacc[mc][nt] * f;
+            const int col = (mc * 16 + 4 * g) ^ ((hr & 15) << 3);
+            st4(sp + col, cvt4(v[0], v[1], v[2], v[3]));
         }
+        if (active && g == 0 && head < a.H) a.lse[(size_t)t * a.H + head] = lse_v[nt];
+    }
+    __syncthreads();
+    // coalesced stores: HT rows of DV bf16, 16 bytes per thread per step
+    const int nh = (a.H - h_wg) < C::HT ? (a.H - h_wg) : C::HT;
+    constexpr int CPR = C::DV / 8;      // chunks per row
+    for (int id = tid; id < nh * CPR; id += NTH) {
+        const int r = id / CPR, ch = id - r * CPR;
+        const __bf16* sp = r < 64 ? s_tile0 + r * C::DV : s_tile1 + (r - 64) * C::DV;
+        *reinterpret_cast<u32x4*>(a.o + ((size_t)t * a.H + h_wg + r) * C::DV + ch * 8) =
+            *reinterpret_cast<const u32x4*>(sp + ((ch * 8) ^ ((r & 15) << 3)));
     }
 }
 
-template <int DQK, int NT>
+template <int DQK, int NW, int NT>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-    dim3 grid(a.T, (a.H + 4 * NT * 16 - 1) / (4 * NT * 16));
-    hipLaunchKernelGGL((fwd_kernel<DQK, NT>), grid, dim3(256), 0, stream, a);
+    constexpr int HT = NW * NT * 16;
+    dim3 grid(a.T, (a.H + HT - 1) / HT);
+    hipLaunchKernelGGL((fwd_kernel<DQK, NW, NT>), grid, dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream) {
+    // head tile: 4 waves x 32 heads (H > 64) or 4 waves x 16 heads
     const bool wide = a.H > 64;
-    if (d_qk == 576) return wide ? launch_fwd_t<576, 2>(a, stream) : launch_fwd_t<576, 1>(a, stream);
-    return wide ? launch_fwd_t<512, 2>(a, stream) : launch_fwd_t<512, 1>(a, stream);
+    if (d_qk == 576)
+        return wide ? launch_fwd_t<576, 4, 2>(a, stream) : launch_fwd_t<576, 4, 1>(a, stream);
+    return wide ? launch_fwd_t<512, 4, 2>(a, stream) : launch_fwd_t<512, 4, 1>(a, stream);
 }
 
 }  // namespace smla
