@@ -30,7 +30,8 @@
  *   - B > 1 batches are expressed by concatenating tokens and KV rows with
  *     global row indices.
  *   - Supported: d_qk in {512, 576}, d_v = 512, 1 <= H <= 128, W >= 1,
- *     S_kv >= 1, T >= 0 (T = 0 is a no-op), scale finite.
+ *     1 <= S_kv <= SMLA_MAX_S_KV, T >= 0 (T = 0 is a no-op), scale finite,
+ *     T * (W rounded up to 64) < 2^31.
  *   - The caller owns every buffer.  The library never allocates or frees
  *     memory and never synchronises: work is enqueued on `stream` (a
  *     hipStream_t; NULL means the null stream) and the call returns.
@@ -48,6 +49,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Largest supported number of KV rows (one 4-byte counter per row in LDS). */
+#define SMLA_MAX_S_KV 40960
 
 typedef enum {
     SMLA_OK = 0,
@@ -100,10 +104,11 @@ size_t smla_bwd_workspace_size(const smla_dims* dims);
  * the sink, dP = dO V^T, dS = P (dP - Delta), and returns
  *   dq         bf16 [T, H, d_qk] out: scale * dS K; 0 for a token with no
  *              valid slot (that token's q, dO, lse and delta are not read)
- *   dkv        fp32 [S_kv, d_qk] out: zeroed, then for every valid slot
- *              dkv[idx, :d_qk] += scale * dS^T q and dkv[idx, :d_v] += P^T dO
- *              (rows never named by a valid slot, e.g. row 0 for -1
- *              sentinels, stay exactly 0)
+ *   dkv        fp32 [S_kv, d_qk] out: row r is the sum, over the valid slots
+ *              that name r taken in token order, of scale * dS^T q (all d_qk
+ *              columns) plus P^T dO (first d_v columns); the order is fixed,
+ *              so dkv is the same bits run to run.  Rows never named by a
+ *              valid slot (e.g. row 0 for -1 sentinels) are exactly 0.
  *   d_sink     fp32 [H] out: -sum_t p_sink[t,h] * delta[t,h] with
  *              p_sink = sigmoid(sink - lse); required iff attn_sink != NULL
  * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16

@@ -13,12 +13,48 @@ smla_status check_dims(const smla_dims* d) {
     if (d->T < 0 || d->S_kv < 1 || d->H < 1 || d->W < 1) return SMLA_ERR_SHAPE;
     if ((d->d_qk != 512 && d->d_qk != 576) || d->d_v != 512 || d->H > 128)
         return SMLA_ERR_UNSUPPORTED;
+    // the backward's index inversion keeps one counter per KV row in LDS, and
+    // flat slot indices t * Wp + j must fit in int32
+    if (d->S_kv > SMLA_MAX_S_KV) return SMLA_ERR_UNSUPPORTED;
+    if ((int64_t)d->T * (((int64_t)d->W + 63) / 64 * 64) >= INT32_MAX) return SMLA_ERR_UNSUPPORTED;
     if (!(d->scale == d->scale) || d->scale == INFINITY || d->scale == -INFINITY)
         return SMLA_ERR_SHAPE;
     return SMLA_OK;
 }
 
 size_t round_up_blk(int W) { return ((size_t)W + smla::BLK - 1) / smla::BLK * smla::BLK; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// tokens per chunk of the backward's index inversion (at most 256 chunks)
+int token_chunk(int T) { return T > 256 ? (T + 255) / 256 : 1; }
+
+// Workspace layout of smla_bwd (each region 256-byte aligned):
+//   P, scale*dS      bf16 [T, H, Wp] each (Wp = W rounded up to 64)
+//   chunk_cnt        int32 [ceil(T / tchunk), S_kv], tchunk = ceil(T / 256)
+//   row_cnt          int32 [S_kv]; row_off int32 [S_kv + 1]
+//   entries          int32 [T * W]
+//   partial          fp32 [T * Wp, d_qk]
+struct WsLayout {
+    size_t p, ds, chunk, cnt, off, ent, part, total;
+};
+
+WsLayout ws_layout(const smla_dims* d) {
+    WsLayout L;
+    const size_t Wp = round_up_blk(d->W);
+    const size_t pd = (size_t)d->T * d->H * Wp * sizeof(uint16_t);
+    const size_t tch = token_chunk(d->T);
+    const size_t nch = ((size_t)d->T + tch - 1) / tch;
+    L.p = 0;
+    L.ds = align256(L.p + pd);
+    L.chunk = align256(L.ds + pd);
+    L.cnt = align256(L.chunk + nch * d->S_kv * sizeof(int32_t));
+    L.off = align256(L.cnt + (size_t)d->S_kv * sizeof(int32_t));
+    L.ent = align256(L.off + ((size_t)d->S_kv + 1) * sizeof(int32_t));
+    L.part = align256(L.ent + (size_t)d->T * d->W * sizeof(int32_t));
+    L.total = align256(L.part + (size_t)d->T * Wp * d->d_qk * sizeof(float));
+    return L;
+}
 
 }  // namespace
 
@@ -74,8 +110,7 @@ smla_status smla_bwd_preprocess(const smla_dims* d, const void* o, const void* d
 
 size_t smla_bwd_workspace_size(const smla_dims* d) {
     if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
-    // P and scale*dS, bf16 [T, H, W rounded up to the 64-slot block]
-    return 2 * (size_t)d->T * d->H * round_up_blk(d->W) * sizeof(uint16_t);
+    return ws_layout(d).total;
 }
 
 smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const void* dO,
@@ -107,8 +142,16 @@ smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const vo
     a.dkv = dkv;
     a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
     a.Wp = (int)round_up_blk(d->W);
-    a.ws_p = static_cast<__bf16*>(workspace);
-    a.ws_ds = a.ws_p + (size_t)d->T * d->H * a.Wp;
+    a.tchunk = token_chunk(d->T);
+    const WsLayout WL = ws_layout(d);
+    char* ws = static_cast<char*>(workspace);
+    a.ws_p = reinterpret_cast<__bf16*>(ws + WL.p);
+    a.ws_ds = reinterpret_cast<__bf16*>(ws + WL.ds);
+    a.chunk_cnt = reinterpret_cast<int*>(ws + WL.chunk);
+    a.row_cnt = reinterpret_cast<int*>(ws + WL.cnt);
+    a.row_off = reinterpret_cast<int*>(ws + WL.off);
+    a.entries = reinterpret_cast<int*>(ws + WL.ent);
+    a.partial = reinterpret_cast<float*>(ws + WL.part);
     a.scale = d->scale;
     a.scale_log2 = d->scale * smla::LOG2E;
     hipError_t e = smla::launch_bwd(d->d_qk, a, d_sink, static_cast<hipStream_t>(stream));

@@ -9,19 +9,26 @@
 //   dQ      = scale * dS K
 //   dKV[idx] += scale * dS^T Q  (all d_qk columns) and P^T dO (first d_v)
 //   d_sink  = -sum_t sigmoid(sink - lse) * Delta
-// Kernels, in launch order:
-//   preprocess   Delta = rowsum(O * dO) in fp32 (separate entry point)
-//   zero_fill    dkv = 0
-//   bwd_main     one workgroup per (token, 64-head tile): gathers the KV tile,
-//                recomputes S, P, dP, dS with bf16 MFMA, accumulates dQ in
-//                registers, and stores P and scale*dS (bf16) to the workspace
-//                for the dKV kernel
+//
+// Kernels, in launch order (preprocess is its own entry point):
+//   rows_count / rows_chunkscan / rows_scan / rows_fill
+//                invert the index lists: every valid (token, slot) is listed
+//                under its KV row, in token order (row r owns the segment
+//                [off[r], off[r+1]) of the list)
+//   bwd_sdp      one workgroup per token, all heads: gathers each 64-slot KV
+//                tile (async, double-buffered), recomputes S, P, dP, dS with
+//                bf16 MFMA and stores P and scale*dS (bf16) to the workspace
+//   bwd_dq       one workgroup per token: gathers the KV tiles again and
+//                accumulates dQ^T = K^T (scale dS)^T in registers
 //   bwd_dkv      one workgroup per token: contracts over all heads,
-//                dKV_blk = (scale*dS)^T Q + P^T dO, and adds it to dkv rows of
-//                the valid slots with fp32 atomics
-//   dsink        one workgroup per head: deterministic sum over tokens
-// An empty row (no valid slot) is a uniform branch: dQ = 0 is written and the
-// token's q, dO, lse and delta are not read.
+//                u = (scale dS)^T q + P^T dO per valid slot (fp32), written to
+//                the slot's row of a [T * Wp, d_qk] partial buffer
+//   dkv_reduce   one wave per KV row: sums the partial rows of the row's list
+//                in token order and writes dkv (unnamed rows get 0)
+//   dsink        one workgroup per head: sum over tokens in token order
+// No fp32 atomics touch dkv: the scatter is a write of per-slot partials plus
+// a streaming reduce.  An empty row (no valid slot) is a uniform branch: dQ = 0
+// is written and the token's q, dO, lse and delta are not read.
 #include "kv_tile.h"
 #include "launch.h"
 
@@ -53,235 +60,592 @@ hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, in
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ p, size_t n) {
-    size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    const size_t stride = (size_t)gridDim.x * 256 * 4;
-    for (; i + 4 <= n; i += stride) *reinterpret_cast<f32x4*>(p + i) = zero4();
-    for (; i < n; ++i) p[i] = 0.f;   // tail (n not a multiple of 4)
+// ---------------------------------------------------------------------------
+// Index inversion: the valid (token, slot) pairs grouped by KV row.
+// Tokens are cut into at most 256 chunks of tchunk consecutive tokens.  rows_count counts,
+// per chunk, the valid slots naming each row (LDS counters); rows_scan turns
+// the counts into row segments and per-chunk offsets inside them; rows_fill
+// walks each chunk's tokens in order and appends every valid slot's flat index
+// t * Wp + j to its row.  A row's list is therefore in token order, so the
+// reduce sums each row in a fixed order: dKV does not depend on scheduling.
+// (Two slots of one token naming the same row carry identical
+// contributions, so their relative order cannot change a sum.)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_i32_kernel(int* __restrict__ p, int v, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = v;
 }
 
+__global__ __launch_bounds__(256) void rows_count_kernel(BwdArgs a) {
+    extern __shared__ int s_cnt[];           // [S_kv]
+    const int c = blockIdx.x;
+    for (int r = threadIdx.x; r < a.S_kv; r += 256) s_cnt[r] = 0;
+    __syncthreads();
+    const int t1 = (c + 1) * a.tchunk < a.T ? (c + 1) * a.tchunk : a.T;
+    for (int t = c * a.tchunk; t < t1; ++t) {
+        const int L = row_length(a.len, t, a.W);
+        for (int j = threadIdx.x; j < L; j += 256) {
+            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j);
+            if (r >= 0) atomicAdd(s_cnt + r, 1);
+        }
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.S_kv; r += 256) a.chunk_cnt[(size_t)c * a.S_kv + r] = s_cnt[r];
+}
+
+// Per row: running offsets over the chunks (chunk_cnt becomes the exclusive
+// prefix inside the row's segment) and the row total.
+__global__ __launch_bounds__(256) void rows_chunkscan_kernel(BwdArgs a) {
+    const int r = (int)blockIdx.x * 256 + threadIdx.x;
+    if (r >= a.S_kv) return;
+    const int nch = (a.T + a.tchunk - 1) / a.tchunk;
+    int run = 0;
+    for (int c = 0; c < nch; ++c) {
+        int* p = a.chunk_cnt + (size_t)c * a.S_kv + r;
+        const int v = *p;
+        *p = run;
+        run += v;
+    }
+    a.row_cnt[r] = run;
+}
+
+// Exclusive scan of the row totals into row_off[0..S_kv] (one workgroup).
+__global__ __launch_bounds__(1024) void rows_scan_kernel(BwdArgs a) {
+    __shared__ int s_part[1024];
+    const int n = a.S_kv;
+    const int per = (n + 1023) / 1024;
+    const int lo = (int)threadIdx.x * per < n ? (int)threadIdx.x * per : n;
+    const int hi = lo + per < n ? lo + per : n;
+    int sum = 0;
+    for (int r = lo; r < hi; ++r) sum += a.row_cnt[r];
+    s_part[threadIdx.x] = sum;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v = (int)threadIdx.x >= d ? s_part[threadIdx.x - d] : 0;
+        __syncthreads();
+        s_part[threadIdx.x] += v;
+        __syncthreads();
+    }
+    int run = s_part[threadIdx.x] - sum;     // exclusive prefix of this thread's rows
+    for (int r = lo; r < hi; ++r) {
+        a.row_off[r] = run;
+        run += a.row_cnt[r];
+    }
+    if (threadIdx.x == 1023) a.row_off[n] = s_part[1023];
+}
+
+__global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
+    extern __shared__ int s_cur[];           // [S_kv]
+    const int c = blockIdx.x;
+    for (int r = threadIdx.x; r < a.S_kv; r += 256)
+        s_cur[r] = a.row_off[r] + a.chunk_cnt[(size_t)c * a.S_kv + r];
+    __syncthreads();
+    const int t1 = (c + 1) * a.tchunk < a.T ? (c + 1) * a.tchunk : a.T;
+    for (int t = c * a.tchunk; t < t1; ++t) {
+        const int L = row_length(a.len, t, a.W);
+        for (int j = threadIdx.x; j < L; j += 256) {
+            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j);
+            if (r >= 0) a.entries[atomicAdd(s_cur + r, 1)] = t * a.Wp + j;
+        }
+        __syncthreads();                     // token order within the chunk
+    }
+}
+
+__device__ __forceinline__ int raw_index_b(const BwdArgs& a, int t, int j) {
+    return a.idx[(size_t)t * a.W + (j < a.W ? j : a.W - 1)];
+}
+
+__device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
+    return (j < L && v >= 0 && v < S_kv) ? v : -1;
+}
+
+// The double-buffered gather loop of the kernels that gather KV tiles:
+// body(tile, rows, b) runs block b from tile 0 (even b) or tile 1 (odd b)
+// while the next block's rows are in flight into the other tile.
+template <int DQK, int NW, typename Body>
+__device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
+                                                int (*s_rows)[BLK], int t, int L, int nblk,
+                                                int wave, int lane, Body&& body) {
+    using Tile = KvTileSwz<DQK>;
+    const int tid = threadIdx.x;
+    if (tid < BLK) {
+        s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
+        s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
+    }
+    __syncthreads();
+    if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], a.kv, wave, lane);
+    for (int b = 0; b < nblk; b += 2) {
+        wait_vmem();
+        __syncthreads();
+        int ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane);
+        body(s_tile0, s_rows[b % 3], b);
+        if (b + 2 < nblk && tid < BLK)
+            s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
+        if (b + 1 >= nblk) break;
+        wait_vmem();
+        __syncthreads();
+        ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
+        __builtin_amdgcn_sched_barrier(0);
+        if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane);
+        body(s_tile1, s_rows[(b + 1) % 3], b + 1);
+        if (b + 3 < nblk && tid < BLK)
+            s_rows[(b + 3) % 3][tid] = valid_row_b(ahead, (b + 3) * BLK + tid, L, a.S_kv);
+    }
+}
 
 // ---------------------------------------------------------------------------
-// Main backward kernel: S, P, dP, dS, dQ for 64 heads of one token.
-// Each of the 4 waves owns 16 heads; Q and dO stay in registers as the B
-// operands of S^T = K Q^T and dP^T = V dO^T; dQ^T accumulates in registers.
+// bwd_sdp: S, P, dP, dS for all heads of one token (NW waves x NT x 16 heads).
+// q and dO stay in registers as the B operands of S^T = K Q^T and
+// dP^T = V dO^T.  Per 64-slot block, two halves of 32 slots.
 // ---------------------------------------------------------------------------
-template <int DQK>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
-    constexpr int DV = 512;
-    constexpr int KS = DQK / 32, KV_ = DV / 32, MC = DQK / 16;
-    using Tile = KvTile<DQK>;
-    __shared__ __attribute__((aligned(16))) __bf16 s_tile[Tile::ELEMS];
-    __shared__ int s_row[BLK];
+template <int DQK, int NW, int NT>
+__device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
+                                          const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
+                                          const bf16x8 (&qop)[NT][DQK / 32],
+                                          const bf16x8 (&dop)[NT][16], const float (&lse2)[NT],
+                                          const float (&dlt)[NT], int t, int h_wave, int b,
+                                          int lane) {
+    using Tile = KvTileSwz<DQK>;
+    constexpr int KS = DQK / 32, KV_ = 16;
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4 sacc[2][NT], dpacc[2][NT];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) { sacc[m][nt] = zero4(); dpacc[m][nt] = zero4(); }
+        bf16x8 kop[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) kop[0][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, 0);
+        // k-steps 0..KS-1 feed S; the first 16 (the V columns) also feed dP
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1;
+            if (ks + 1 < KS) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    kop[cur ^ 1][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, ks + 1);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    sacc[m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[m][nt]);
+                    if (ks < KV_) dpacc[m][nt] = mfma16(kop[cur][m], dop[nt][ks], dpacc[m][nt]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // P = 2^(s * scale * log2 e - LSE_tot * log2 e), masked; dS' = scale P (dP - Delta)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            f32x4 pv[2], dsv[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
+                    const float p = ok ? fast_exp2(sacc[m][nt][i] * a.scale_log2 - lse2[nt]) : 0.f;
+                    pv[m][i] = p;
+                    dsv[m][i] = p * (dpacc[m][nt][i] - dlt[nt]) * a.scale;
+                }
+            }
+            if (head < a.H) {
+                const size_t base = ((size_t)t * a.H + head) * a.Wp + b * BLK + half * 32 + 4 * g;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    st4(a.ws_p + base + m * 16, cvt4(pv[m][0], pv[m][1], pv[m][2], pv[m][3]));
+                    st4(a.ws_ds + base + m * 16, cvt4(dsv[m][0], dsv[m][1], dsv[m][2], dsv[m][3]));
+                }
+            }
+        }
+    }
+}
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int DQK, int NW, int NT>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
+    using Tile = KvTileSwz<DQK>;
+    constexpr int KS = DQK / 32, HT = NW * NT * 16;
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
+    __shared__ int s_rows[3][BLK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
     const int t = a.T - 1 - (int)blockIdx.x;
-    const int head = (int)blockIdx.y * 64 + wave * 16 + n;
-    const bool active = (int)blockIdx.y * 64 + wave * 16 < a.H;   // wave-uniform
-    const bool hv = head < a.H;
+    const int h_wave = (int)blockIdx.y * HT + wave * NT * 16;
+    const bool active = h_wave < a.H;
+    const int L = row_length(a.len, t, a.W);
+    const int nblk = (L + BLK - 1) / BLK;
+    if (nblk == 0) return;                       // uniform: nothing to store
+
+    bf16x8 qop[NT][KS], dop[NT][16];
+    float lse2[NT], dlt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int head = h_wave + nt * 16 + n;
+        const bool hv = head < a.H;
+        const size_t row = (size_t)t * a.H + (hv ? head : 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = hv ? ld8(a.q + row * DQK + 32 * ks + 8 * g) : zero8();
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) dop[nt][ks] = hv ? ld8(a.dO + row * 512 + 32 * ks + 8 * g) : zero8();
+        lse2[nt] = 0.f;
+        dlt[nt] = 0.f;
+        if (hv) {
+            const float l = a.lse[row];
+            const float lt = a.sink ? glae(l, a.sink[head]) : l;
+            lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
+            dlt[nt] = a.delta[row];
+        }
+    }
+    const typename Tile::Lane TL = Tile::lane_bases(lane);
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
+                             [&](const __bf16* tile, const int* rows, int b) {
+                                 if (active)
+                                     sdp_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, dlt, t,
+                                                            h_wave, b, lane);
+                             });
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq: dQ^T = K^T (scale dS)^T for all heads of one token.  NW waves; wave
+// w owns NT x 16 heads and 1/CS of the d_qk columns (CS column groups, the
+// waves of one head group are adjacent).
+// ---------------------------------------------------------------------------
+template <int DQK, int NW, int NT, int CS>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
+    using Tile = KvTileSwz<DQK>;
+    constexpr int MCW = DQK / 16 / CS;                 // column tiles per wave
+    constexpr int HT = NW / CS * NT * 16;              // heads per workgroup
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
+    __shared__ int s_rows[3][BLK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int t = a.T - 1 - (int)blockIdx.x;
+    const int h_wave = (int)blockIdx.y * HT + (wave / CS) * NT * 16;
+    const int mc0 = (wave % CS) * MCW;
+    const bool active = h_wave < a.H;
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
 
-    bf16x8 qop[KS], dop[KV_];
-    float lse_log2 = 0.f, dlt = 0.f;
-    if (nblk > 0) {
-        const int hh = hv ? head : 0;
-        const __bf16* qp = a.q + ((size_t)t * a.H + hh) * DQK + 8 * g;
-        const __bf16* dp = a.dO + ((size_t)t * a.H + hh) * DV + 8 * g;
+    f32x4 acc[MCW][NT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[ks] = hv ? ld8(qp + 32 * ks) : zero8();
+    for (int mc = 0; mc < MCW; ++mc)
 #pragma unroll
-        for (int ks = 0; ks < KV_; ++ks) dop[ks] = hv ? ld8(dp + 32 * ks) : zero8();
-        if (hv) {
-            const float l = a.lse[(size_t)t * a.H + head];
-            const float lt = a.sink ? glae(l, a.sink[head]) : l;
-            lse_log2 = lt * LOG2E;    // +inf for a saturating sink: every P is 0
-            dlt = a.delta[(size_t)t * a.H + head];
-        }
-    }
+        for (int nt = 0; nt < NT; ++nt) acc[mc][nt] = zero4();
+    const typename Tile::Lane TL = Tile::lane_bases(lane);
 
-    f32x4 dqacc[MC];
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
+                             [&](const __bf16* tile, const int* rows, int b) {
+        (void)rows;
+        if (!active) return;
+        // (scale dS)^T as B operands: lane (g, n) holds 8 slots of head n in
+        // the slot order of slot_op: 32kk + 4g + j (j < 4), 32kk + 16 + 4g + j - 4
+        bf16x8 dsop[2][NT];
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) dqacc[mc] = zero4();
-
-    for (int b = 0; b < nblk; ++b) {
-        __syncthreads();
-        Tile::load_rows(s_row, a.idx, t, a.W, L, a.S_kv, b);
-        __syncthreads();
-        Tile::gather(s_tile, s_row, a.kv);
-        __syncthreads();
-        if (!active) continue;
-
-        f32x4 sacc[4], dpacc[4];
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            const bool hv = head < a.H;
+            const __bf16* src = a.ws_ds + ((size_t)t * a.H + (hv ? head : 0)) * a.Wp + b * BLK + 4 * g;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) { sacc[mt] = zero4(); dpacc[mt] = zero4(); }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                sacc[mt] = mfma16(Tile::row_op(s_tile, mt * 16, ks * 32, lane), qop[ks], sacc[mt]);
-#pragma unroll
-        for (int ks = 0; ks < KV_; ++ks)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                dpacc[mt] = mfma16(Tile::row_op(s_tile, mt * 16, ks * 32, lane), dop[ks], dpacc[mt]);
-
-        // P and scale*dS; invalid slots (and padded heads) give exactly 0
-        f32x4 pv[4], dsv[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = hv && s_row[mt * 16 + 4 * g + i] >= 0;
-                const float p = ok ? fast_exp2(sacc[mt][i] * a.scale_log2 - lse_log2) : 0.f;
-                pv[mt][i] = p;
-                dsv[mt][i] = p * (dpacc[mt][i] - dlt) * a.scale;
+            for (int kk = 0; kk < 2; ++kk) {
+                if (hv) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 32 * kk);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 32 * kk + 16);
+                    dsop[kk][nt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                } else {
+                    dsop[kk][nt] = zero8();
+                }
             }
         }
-        if (hv) {
-            const size_t base = ((size_t)t * a.H + head) * a.Wp + b * BLK + 4 * g;
+        bf16x8 kop[2][2];
+        kop[0][0] = Tile::slot_op(tile, TL, 0, mc0);
+        kop[0][1] = Tile::slot_op(tile, TL, 32, mc0);
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                st4(a.ws_p + base + mt * 16, cvt4(pv[mt][0], pv[mt][1], pv[mt][2], pv[mt][3]));
-                st4(a.ws_ds + base + mt * 16, cvt4(dsv[mt][0], dsv[mt][1], dsv[mt][2], dsv[mt][3]));
+        for (int mc = 0; mc < MCW; ++mc) {
+            const int cur = mc & 1;
+            if (mc + 1 < MCW) {
+                kop[cur ^ 1][0] = Tile::slot_op(tile, TL, 0, mc0 + mc + 1);
+                kop[cur ^ 1][1] = Tile::slot_op(tile, TL, 32, mc0 + mc + 1);
             }
-        }
-        const bf16x8 dsop0 = cvt8(dsv[0], dsv[1]);
-        const bf16x8 dsop1 = cvt8(dsv[2], dsv[3]);
-        // dQ^T += K^T (scale dS)^T
 #pragma unroll
-        for (int mc = 0; mc < MC; ++mc) {
-            dqacc[mc] = mfma16(Tile::slot_op(s_tile, 0, mc * 16, lane), dsop0, dqacc[mc]);
-            dqacc[mc] = mfma16(Tile::slot_op(s_tile, 32, mc * 16, lane), dsop1, dqacc[mc]);
+            for (int nt = 0; nt < NT; ++nt) {
+                acc[mc][nt] = mfma16(kop[cur][0], dsop[0][nt], acc[mc][nt]);
+                acc[mc][nt] = mfma16(kop[cur][1], dsop[1][nt], acc[mc][nt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    });
 
-    if (!active || !hv) return;
-    __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 4 * g;
+    if (!active) return;
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc)
-        st4(dqp + mc * 16, cvt4(dqacc[mc][0], dqacc[mc][1], dqacc[mc][2], dqacc[mc][3]));
+    for (int nt = 0; nt < NT; ++nt) {
+        const int head = h_wave + nt * 16 + n;
+        if (head >= a.H) continue;
+        __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 16 * mc0 + 4 * g;
+#pragma unroll
+        for (int mc = 0; mc < MCW; ++mc)
+            st4(dqp + mc * 16, cvt4(acc[mc][nt][0], acc[mc][nt][1], acc[mc][nt][2], acc[mc][nt][3]));
+    }
 }
 
 // ---------------------------------------------------------------------------
-// dKV kernel: per token and 64-slot block,
-//   dKV_blk[slot][c] = sum_h (scale dS)[h][slot] q[h][c] + P[h][slot] dO[h][c]
-// Contraction over heads (padded to 128).  Wave w owns columns
-// [w * DQK/4, (w+1) * DQK/4); q and dO for those columns are held in registers
-// with heads in-lane (loaded once per token through an LDS transpose).
+// bwd_dkv: per token and 64-slot block,
+//   u[slot][c] = sum_h (scale dS)[h][slot] q[h][c] + P[h][slot] dO[h][c]
+// computed as u^T = q^T (scale dS) + dO^T P, a contraction over heads (HK
+// k-steps of 32 heads).  Wave w owns the columns [w * DQK/4, (w+1) * DQK/4);
+// q and dO for those columns stay in registers with heads in-lane, staged once
+// per token through LDS with asynchronous loads (two buffers in flight).  The
+// P / dS tiles of the next block load asynchronously while the current block
+// is computed.  Each lane ends up holding 4 consecutive columns of u for one
+// slot and writes them as one 16-byte store into the slot's row of the
+// [T * Wp, d_qk] partial buffer.
 // ---------------------------------------------------------------------------
-template <int DQK>
+
+// P or scale*dS tile: [HP heads][64 slots] bf16, 128-byte rows, chunk c of row
+// h stored at c ^ pf(h) so that the transposed reads (4 consecutive heads x 32
+// bytes per 16 lanes, two lane groups 8 heads apart per 32 lanes) avoid bank
+// conflicts.
+__device__ __forceinline__ int pf(int h) { return (((h >> 1) & 1) << 1) | (((h >> 3) & 1) << 2); }
+
+template <int D, int NW>
+__device__ __forceinline__ void stage_rows_async(__bf16* dst, const __bf16* src_rows, int nrows_valid,
+                                                 int wave_s, int lane) {
+    // 32 rows x D columns; rows >= nrows_valid repeat the last valid row
+    constexpr int CH = D / 8;
+    constexpr int INSTR = 32 * CH / 64;
+    static_assert(INSTR % NW == 0, "pieces must split evenly over the waves");
+    int lv;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lv) : "v"(lane));
+#pragma unroll
+    for (int k = 0; k < INSTR / NW; ++k) {
+        const int i = k * NW + wave_s;
+        const int pos = i * 64 + lv;
+        const int row = pos / CH;
+        const int pc = pos - row * CH;
+        const int rr = row < nrows_valid ? row : nrows_valid - 1;
+        const __bf16* src = src_rows + (size_t)rr * D + ((pc ^ SwzF<D>::f(row)) << 3);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + i * 512), 16, 0, 0);
+    }
+}
+
+// B-operand read of staged rows: lane (g, n) gets rows 8g..8g+7 (as two
+// transposed 4-row reads) of column c0 + n.
+template <int D>
+__device__ __forceinline__ bf16x8 stage_op(const __bf16* stage, int c0, int lane) {
+    const int g = lane >> 4, w = lane & 15;
+    const int row = 8 * g + (w >> 2);
+    const int col = c0 + 4 * (w & 3);
+    const int e0 = row * D + ((((col >> 3) ^ SwzF<D>::f(row))) << 3) + (col & 7);
+    const int e1 = (row + 4) * D + ((((col >> 3) ^ SwzF<D>::f(row + 4))) << 3) + (col & 7);
+    return cat44(lds_tr4(stage + e0), lds_tr4(stage + e1));
+}
+
+// Issue the loads of the [P | scale dS] tiles of block b into buf (rows
+// h < H of each; pieces of 8 head rows = 1 KB).  No wait here.
+template <int HP, int NW>
+__device__ __forceinline__ void pd_tiles_async(const BwdArgs& a, __bf16* buf, int t, int b,
+                                               int wave_s, int lane) {
+    const int np = (a.H + 7) >> 3;                 // pieces per tile
+    const int row_in = lane >> 3, pc = lane & 7;
+    for (int i = wave_s; i < 2 * np; i += NW) {
+        const int which = i >= np;                 // 0: P, 1: scale dS
+        const int k = i - which * np;
+        const int h = 8 * k + row_in;
+        if (h < a.H) {
+            const __bf16* src = (which ? a.ws_ds : a.ws_p) + ((size_t)t * a.H + h) * a.Wp + b * BLK +
+                                ((pc ^ pf(h)) << 3);
+            __builtin_amdgcn_global_load_lds((const void*)src,
+                                             (lds_void*)(buf + which * HP * BLK + 8 * k * BLK), 16, 0, 0);
+        }
+    }
+}
+
+// B-operand read of a P / dS tile: lane (g, n) gets heads h0 + 8g .. +7 of
+// slot s0 + n.
+__device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int lane) {
+    const int g = lane >> 4, w = lane & 15;
+    const int h = h0 + 8 * g + (w >> 2);
+    const int col = s0 + 4 * (w & 3);
+    const int e0 = h * BLK + ((((col >> 3) ^ pf(h))) << 3) + (col & 7);
+    const int e1 = (h + 4) * BLK + ((((col >> 3) ^ pf(h + 4))) << 3) + (col & 7);
+    return cat44(lds_tr4(tile + e0), lds_tr4(tile + e1));
+}
+
+template <int DQK, int HK>
+__device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd,
+                                          const bf16x8 (&qB)[HK][DQK / 64],
+                                          const bf16x8 (&dB)[HK][DQK / 64], int t, int b,
+                                          int c_wave, int lane) {
+    constexpr int DV = 512;
+    constexpr int NTC = DQK / 64;
+    constexpr int HP = 32 * HK;
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        f32x4 acc[NTC][2];
+#pragma unroll
+        for (int nt = 0; nt < NTC; ++nt) { acc[nt][0] = zero4(); acc[nt][1] = zero4(); }
+#pragma unroll
+        for (int hk = 0; hk < HK; ++hk) {
+            bf16x8 bds[2], bp[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                bp[m] = pd_op(pd, 32 * hk, (2 * half + m) * 16, lane);
+                bds[m] = pd_op(pd + HP * BLK, 32 * hk, (2 * half + m) * 16, lane);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTC; ++nt) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    acc[nt][m] = mfma16(qB[hk][nt], bds[m], acc[nt][m]);
+                    if (c_wave + 16 * nt < DV) acc[nt][m] = mfma16(dB[hk][nt], bp[m], acc[nt][m]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot
+        // 32 half + 16 m + n; every slot of the block is written (invalid slots
+        // carry P = dS = 0, so u = 0, and the row lists never name them)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int slot = (2 * half + m) * 16 + n;
+            float* dst = a.partial + ((size_t)t * a.Wp + b * BLK + slot) * DQK + c_wave + 4 * g;
+#pragma unroll
+            for (int nt = 0; nt < NTC; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt][m];
+        }
+    }
+}
+
+template <int DQK, int HK>
 __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int DV = 512;
+    constexpr int NW = 4;
     constexpr int CW = DQK / 4;          // columns per wave
     constexpr int NTC = CW / 16;         // 16-column tiles per wave
-    constexpr int HK = 4;                // k-steps of 32 heads (H padded to 128)
-    constexpr int QRS = DQK + 8;         // staging row stride (q rows)
-    constexpr int PRS = BLK + 8;         // P / dS tile row stride
-    __shared__ __attribute__((aligned(16))) __bf16 s_stage[32 * QRS];
-    __shared__ __attribute__((aligned(16))) __bf16 s_ds[128 * PRS];
-    __shared__ __attribute__((aligned(16))) __bf16 s_p[128 * PRS];
-    __shared__ int s_row[BLK];
+    constexpr int HP = 32 * HK;          // heads padded
+    __shared__ __attribute__((aligned(16))) __bf16 s_st0[32 * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 s_st1[32 * DQK];
+    __shared__ __attribute__((aligned(16))) __bf16 s_pd0[2 * HP * BLK];   // [P | dS], even blocks
+    __shared__ __attribute__((aligned(16))) __bf16 s_pd1[2 * HP * BLK];   // [P | dS], odd blocks
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, n = lane & 15;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = a.T - 1 - (int)blockIdx.x;
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
     if (nblk == 0) return;                 // uniform: an empty row adds nothing
     const int c_wave = wave * CW;
 
-    // q and dO with heads in-lane: lane (g, n) of k-step hk, column tile nt holds
-    // X[32hk + 8g + j][c_wave + 16nt + n], j = 0..7
-    bf16x8 qB[HK][NTC], dB[HK][NTC];
-#pragma unroll
-    for (int hk = 0; hk < HK; ++hk) {
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int D = pass == 0 ? DQK : DV;
-            const __bf16* src = pass == 0 ? a.q : a.dO;
-            __syncthreads();
-            // stage rows (heads) 32hk .. 32hk+31 of this token, zeros past H
-            for (int id = tid; id < 32 * (D / 8); id += 256) {
-                const int r = id / (D / 8), ch = id - r * (D / 8);
-                const int h = 32 * hk + r;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (h < a.H) v = *reinterpret_cast<const u32x4*>(src + ((size_t)t * a.H + h) * D + ch * 8);
-                *reinterpret_cast<u32x4*>(s_stage + r * QRS + ch * 8) = v;
-            }
-            __syncthreads();
-            const int w = lane & 15;
-            const int row = 8 * g + (w >> 2);
-#pragma unroll
-            for (int nt = 0; nt < NTC; ++nt) {
-                const int col = c_wave + 16 * nt + 4 * (w & 3);
-                bf16x8 v = zero8();
-                if (pass == 0 || c_wave + 16 * nt < DV) {
-                    const bf16x4 lo = lds_tr4(s_stage + row * QRS + col);
-                    const bf16x4 hi = lds_tr4(s_stage + (row + 4) * QRS + col);
-                    v = cat44(lo, hi);
-                }
-                if (pass == 0) qB[hk][nt] = v; else dB[hk][nt] = v;
-            }
+    // heads past H: their P / dS tile rows stay zero (never loaded)
+    if (HP > a.H) {
+        for (int i = tid; i < 2 * HP * BLK / 8; i += 256) {
+            reinterpret_cast<u32x4*>(s_pd0)[i] = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4*>(s_pd1)[i] = u32x4{0u, 0u, 0u, 0u};
         }
     }
 
-    for (int b = 0; b < nblk; ++b) {
+    // ---- q and dO with heads in-lane: lane (g, n) of k-step hk, column tile
+    // nt holds X[32hk + 8g + j][c_wave + 16nt + n], j = 0..7.  Staged in 2*HK
+    // pieces of 32 head rows (rows past H repeat row H-1: their P and dS are
+    // zero), two buffers in flight.
+    bf16x8 qB[HK][NTC], dB[HK][NTC];
+    auto issue = [&](int piece, __bf16* buf) {
+        const int hk = piece >> 1;
+        const int nv = a.H - 32 * hk;
+        const size_t row0 = (size_t)t * a.H + 32 * hk;
+        if ((piece & 1) == 0) stage_rows_async<DQK, NW>(buf, a.q + row0 * DQK, nv, wave, lane);
+        else stage_rows_async<DV, NW>(buf, a.dO + row0 * DV, nv, wave, lane);
+    };
+    __syncthreads();                      // zero-fill done before any tile load lands
+    issue(0, s_st0);
+#pragma unroll
+    for (int piece = 0; piece < 2 * HK; ++piece) {
+        __bf16* cur = (piece & 1) ? s_st1 : s_st0;
+        __bf16* nxt = (piece & 1) ? s_st0 : s_st1;
+        wait_vmem();
         __syncthreads();
-        KvTile<DQK>::load_rows(s_row, a.idx, t, a.W, L, a.S_kv, b);
-        // P and scale*dS tiles [head][slot] for this block, zeros past H
-        for (int id = tid; id < 2 * 128 * (BLK / 8); id += 256) {
-            const int which = id / (128 * (BLK / 8));
-            const int rem = id - which * 128 * (BLK / 8);
-            const int h = rem / (BLK / 8), ch = rem - h * (BLK / 8);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (h < a.H) {
-                const __bf16* src = which ? a.ws_p : a.ws_ds;
-                v = *reinterpret_cast<const u32x4*>(src + ((size_t)t * a.H + h) * a.Wp + b * BLK + ch * 8);
-            }
-            *reinterpret_cast<u32x4*>((which ? s_p : s_ds) + h * PRS + ch * 8) = v;
+        if (piece + 1 < 2 * HK) issue(piece + 1, nxt);
+        else pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
+        const int hk = piece >> 1;
+#pragma unroll
+        for (int nt = 0; nt < NTC; ++nt) {
+            const int c0 = c_wave + 16 * nt;
+            if ((piece & 1) == 0) qB[hk][nt] = stage_op<DQK>(cur, c0, lane);
+            else dB[hk][nt] = c0 < DV ? stage_op<DV>(cur, c0, lane) : zero8();
         }
-        __syncthreads();
+    }
 
-        f32x4 acc[4][NTC];
+    // ---- blocks: [P | dS] tiles double-buffered
+    for (int b = 0; b < nblk; b += 2) {
+        wait_vmem();
+        __syncthreads();
+        if (b + 1 < nblk) pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
+        dkv_block<DQK, HK>(a, s_pd0, qB, dB, t, b, c_wave, lane);
+        if (b + 1 >= nblk) break;
+        wait_vmem();
+        __syncthreads();
+        if (b + 2 < nblk) pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
+        dkv_block<DQK, HK>(a, s_pd1, qB, dB, t, b + 1, c_wave, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dkv_reduce: dkv[r] = sum of the partial rows listed in r's segment, in list
+// (token) order.
+// One wave per KV row; lane l owns columns 4l..4l+3 (+256, +512 as needed).
+// ---------------------------------------------------------------------------
+template <int DQK>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(BwdArgs a) {
+    constexpr int NV = (DQK / 4 + 63) / 64;   // float4 per lane (3 for 576, 2 for 512)
+    const int r = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= a.S_kv) return;
+    const int lo = a.row_off[r], hi = a.row_off[r + 1];
+    f32x4 acc[NV];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+    for (int v = 0; v < NV; ++v) acc[v] = zero4();
+    int e = lo;
+    for (; e + 2 <= hi; e += 2) {
+        const float* p0 = a.partial + (size_t)a.entries[e] * DQK;
+        const float* p1 = a.partial + (size_t)a.entries[e + 1] * DQK;
+        f32x4 x0[NV], x1[NV];
 #pragma unroll
-            for (int nt = 0; nt < NTC; ++nt) acc[mt][nt] = zero4();
-        const int w = lane & 15;
-#pragma unroll
-        for (int hk = 0; hk < HK; ++hk) {
-            const int row = 32 * hk + 8 * g + (w >> 2);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int col = mt * 16 + 4 * (w & 3);
-                // A operand [slot][head]: lane (g, slot n) holds heads 32hk+8g+j
-                const bf16x8 aop_ds = cat44(lds_tr4(s_ds + row * PRS + col),
-                                            lds_tr4(s_ds + (row + 4) * PRS + col));
-                const bf16x8 aop_p = cat44(lds_tr4(s_p + row * PRS + col),
-                                           lds_tr4(s_p + (row + 4) * PRS + col));
-#pragma unroll
-                for (int nt = 0; nt < NTC; ++nt) {
-                    acc[mt][nt] = mfma16(aop_ds, qB[hk][nt], acc[mt][nt]);
-                    if (c_wave + 16 * nt < DV) acc[mt][nt] = mfma16(aop_p, dB[hk][nt], acc[mt][nt]);
-                }
+        for (int v = 0; v < NV; ++v) {
+            const int c = 4 * (lane + 64 * v);
+            x0[v] = zero4();
+            x1[v] = zero4();
+            if (c < DQK) {
+                x0[v] = *reinterpret_cast<const f32x4*>(p0 + c);
+                x1[v] = *reinterpret_cast<const f32x4*>(p1 + c);
             }
         }
-        // scatter-add to the KV rows of the valid slots
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int v = 0; v < NV; ++v) { acc[v] += x0[v]; acc[v] += x1[v]; }
+    }
+    if (e < hi) {
+        const float* p0 = a.partial + (size_t)a.entries[e] * DQK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = s_row[mt * 16 + 4 * g + i];
-                if (r >= 0) {
-                    float* dst = a.dkv + (size_t)r * DQK + c_wave + n;
-#pragma unroll
-                    for (int nt = 0; nt < NTC; ++nt) unsafeAtomicAdd(dst + 16 * nt, acc[mt][nt][i]);
-                }
-            }
+        for (int v = 0; v < NV; ++v) {
+            const int c = 4 * (lane + 64 * v);
+            if (c < DQK) acc[v] += *reinterpret_cast<const f32x4*>(p0 + c);
         }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int c = 4 * (lane + 64 * v);
+        if (c < DQK) *reinterpret_cast<f32x4*>(a.dkv + (size_t)r * DQK + c) = acc[v];
     }
 }
 
@@ -315,20 +679,51 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
     if (threadIdx.x == 0) d_sink[h] = -s_part[0];
 }
 
+template <int DQK, int HK>
+static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.T), dim3(256), 0, stream, a);
+}
+
+template <int DQK>
+static void launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+    const int hk = (a.H + 31) / 32;
+    if (a.H > 64) {
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 2>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.T, 1), dim3(512), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+    }
+    switch (hk) {
+        case 1: launch_dkv_t<DQK, 1>(a, stream); break;
+        case 2: launch_dkv_t<DQK, 2>(a, stream); break;
+        case 3: launch_dkv_t<DQK, 3>(a, stream); break;
+        default: launch_dkv_t<DQK, 4>(a, stream); break;
+    }
+    hipLaunchKernelGGL((dkv_reduce_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
+}
+
 hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream) {
-    const size_t n_dkv = (size_t)a.S_kv * d_qk;
-    const size_t want = (n_dkv + 1023) / 1024;
-    const int zb = (int)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(zb), dim3(256), 0, stream, a.dkv, n_dkv);
     if (a.T > 0) {
-        dim3 gmain(a.T, (a.H + 63) / 64);
-        if (d_qk == 576) {
-            hipLaunchKernelGGL(bwd_main_kernel<576>, gmain, dim3(256), 0, stream, a);
-            hipLaunchKernelGGL(bwd_dkv_kernel<576>, dim3(a.T), dim3(256), 0, stream, a);
-        } else {
-            hipLaunchKernelGGL(bwd_main_kernel<512>, gmain, dim3(256), 0, stream, a);
-            hipLaunchKernelGGL(bwd_dkv_kernel<512>, dim3(a.T), dim3(256), 0, stream, a);
-        }
+        const int nch = (a.T + a.tchunk - 1) / a.tchunk;
+        const size_t lds = (size_t)a.S_kv * sizeof(int);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute(reinterpret_cast<const void*>(rows_fill_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(rows_count_kernel, dim3(nch), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);
+        if (d_qk == 576) launch_bwd_t<576>(a, stream);
+        else launch_bwd_t<512>(a, stream);
+    } else {
+        // no tokens: dkv is all zeros
+        const size_t n = (size_t)a.S_kv * d_qk;
+        const size_t want = (n + 255) / 256;
+        const int fb = (int)(want < 4096 ? want : 4096);
+        hipLaunchKernelGGL(fill_i32_kernel, dim3(fb), dim3(256), 0, stream,
+                           reinterpret_cast<int*>(a.dkv), 0, n);
     }
     if (a.sink != nullptr)
         hipLaunchKernelGGL(dsink_kernel, dim3(a.H), dim3(256), 0, stream, a.lse, a.delta, a.sink,

@@ -29,9 +29,16 @@ struct BwdArgs {
     const float* sink;
     __bf16* dq;
     float* dkv;
+    // workspace
     __bf16* ws_p;     // [T, H, Wp] bf16: P
     __bf16* ws_ds;    // [T, H, Wp] bf16: scale * dS
+    int* chunk_cnt;   // [ceil(T / tchunk), S_kv]: per token chunk, slots naming each row
+    int* row_cnt;     // [S_kv]: valid slots naming each KV row
+    int* row_off;     // [S_kv + 1]: segment starts of the row-grouped list
+    int* entries;     // [T * W]: flat slot indices t * Wp + j, grouped by row
+    float* partial;   // [T * Wp, d_qk] fp32: per-slot dKV contributions
     int T, S_kv, H, W, Wp;
+    int tchunk;       // tokens per chunk of the index inversion
     float scale, scale_log2;
 };
 

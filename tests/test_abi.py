@@ -53,6 +53,7 @@ def _dims(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d_qk=128), 3), (dict(d_v=256), 3), (dict(H=129), 3), (dict(H=0), 2),
+    (dict(S_kv=40961), 3),
     (dict(W=0), 2), (dict(S_kv=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2),
 ])
 def test_fwd_rejects_bad_dims(lib, kw, code):
@@ -77,9 +78,26 @@ def test_empty_problem_is_a_no_op(lib):
     assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == 0
 
 
+def _ws_expected(T, S_kv, H, d_qk, W):
+    """The documented workspace layout of smla_bwd, each region 256-byte aligned."""
+    a = lambda x: (x + 255) // 256 * 256
+    Wp = (W + 63) // 64 * 64
+    pd = T * H * Wp * 2
+    off = a(pd)                          # P
+    off = a(off + pd)                    # scale * dS
+    tch = (T + 255) // 256 if T > 256 else 1
+    off = a(off + (T + tch - 1) // tch * S_kv * 4)   # chunk counts
+    off = a(off + S_kv * 4)              # row counts
+    off = a(off + (S_kv + 1) * 4)        # row offsets
+    off = a(off + T * W * 4)             # row lists
+    return a(off + T * Wp * d_qk * 4)    # partials
+
+
 def test_workspace_size_and_check(lib):
     d = _dims(lib, T=3, H=5, W=70)
-    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == 2 * 3 * 5 * 128 * 2
+    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == _ws_expected(3, 8, 5, 576, 70)
+    d2 = _dims(lib, T=300, S_kv=1000, H=128, d_qk=512, W=640)
+    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d2)) == _ws_expected(300, 1000, 128, 512, 640)
     p = ctypes.c_void_p(0x1000)
     st = lib.LIB.smla_bwd(ctypes.byref(d), p, p, p, p, p, p, None, None, p, p, None, p,
                           ctypes.c_size_t(10), None)
