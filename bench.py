@@ -17,6 +17,7 @@ one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,14 +40,33 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv4_flash_h128")
-    ap.add_argument("--cpu-tokens", type=int, default=384,
+    ap.add_argument("--cpu-tokens", type=int, default=2560,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size (1 GiB read + 1 GiB written per launch), to
+    scale the FETCH_SIZE / WRITE_SIZE counters of the same profiler runs."""
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
               "(no collectives, no sharding).  Run with --gpus 1.", file=sys.stderr)
@@ -75,6 +95,15 @@ def main():
     ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)   # the library launches on this stream
 
+    # events: [fwd start, fwd end = preprocess start, preprocess end = bwd stage 0, bwd stages...]
+    nb = len(_lib.BWD_STAGES) + 1
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 + nb)]
+        for e in evs:          # materialise the HIP event handles
+            e.record(stream)
+        return evs
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -82,18 +111,15 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         _lib.smla_bwd_preprocess(o, dO, delta=delta, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
         _lib.smla_bwd(q, kv, dO, lse, delta, idx, length, sink, p.scale, dq=dq, dkv=dkv,
-                      d_sink=d_sink, workspace=ws, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+                      d_sink=d_sink, workspace=ws, stream=stream,
+                      stage_events=None if ev is None else ev[2:])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -101,30 +127,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    pre_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    names = ["fwd", "preprocess"] + list(_lib.BWD_STAGES)
+    stage_ms = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, nm in enumerate(names)}
+    step_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
     ms_per_step = wall * 1e3 / args.steps
     total_flop = fwd_flop + bwd_flop
     value = total_flop / (ms_per_step * 1e-3) / 1e12
-
-    # dominant kernel: the forward kernel is the only kernel of smla_fwd, so the
-    # events around smla_fwd bracket it exactly
-    fwd_s = float(np.mean(fwd_ms)) * 1e-3
-    achieved_gbs = gathered / fwd_s / 1e9
-    roofline = {
-        "kernel": "fwd_kernel<576,2> (smla_fwd)",
-        "bound": "hbm",
-        "achieved": round(achieved_gbs, 1),
-        "peak": PEAK_HBM_GBS,
-        "unit": "GB/s",
-        "frac": round(achieved_gbs / PEAK_HBM_GBS, 4),
-        "traffic": None,
-        "algorithmic_bytes_per_launch": int(gathered),
-        "mfma_tflops": round(fwd_flop / fwd_s / 1e12, 1),
-        "mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
-    }
+    work = stage_work(p, n_valid)
+    dominant = max(stage_ms, key=lambda k: stage_ms[k])
+    roofline = roofline_for(dominant, stage_ms[dominant] * 1e-3, work[dominant])
+    fwd_s = stage_ms["fwd"] * 1e-3
 
     cpu = None
     if not args.no_cpu:
@@ -151,19 +164,88 @@ def main():
             "sink": p.attn_sink is not None, "valid_slots": n_valid,
         },
         "detail": {
-            "fwd_us": round(float(np.mean(fwd_ms)) * 1e3, 1),
-            "bwd_preprocess_us": round(float(np.mean(pre_ms)) * 1e3, 1),
-            "bwd_us": round(float(np.mean(bwd_ms)) * 1e3, 1),
-            "step_us_events": round(float(np.mean(step_ms)) * 1e3, 1),
+            "stage_us": {k: round(v * 1e3, 1) for k, v in stage_ms.items()},
+            "fwd_us": round(stage_ms["fwd"] * 1e3, 1),
+            "bwd_us": round((step_ms - stage_ms["fwd"]) * 1e3, 1),
+            "step_us_events": round(step_ms * 1e3, 1),
             "fwd_tflops": round(fwd_flop / fwd_s / 1e12, 1),
-            "bwd_tflops": round(bwd_flop / (float(np.mean(pre_ms + bwd_ms)) * 1e-3) / 1e12, 1),
+            "bwd_tflops": round(bwd_flop / ((step_ms - stage_ms["fwd"]) * 1e-3) / 1e12, 1),
             "fwd_gathered_tbs": round(gathered / fwd_s / 1e12, 3),
+            "fwd_gathered_frac_hbm": round(gathered / fwd_s / 1e9 / PEAK_HBM_GBS, 4),
+            "fwd_mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
             "fwd_flop": fwd_flop, "bwd_flop": bwd_flop, "gathered_bytes_fwd": gathered,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+# kernel-name fragment of each timed stage (for the counter profile)
+STAGE_KERNEL = {"fwd": "fwd_kernel", "preprocess": "preprocess_kernel",
+                "index_inversion": "rows_", "sdp": "bwd_sdp_kernel", "dq": "bwd_dq_kernel",
+                "dkv": "bwd_dkv_kernel", "dkv_reduce": "dkv_reduce_kernel",
+                "dsink": "dsink_kernel"}
+
+
+def stage_work(p, n):
+    """Algorithmic work per launch of each stage: (FLOP, bytes).  n = valid
+    (token, slot) pairs.  Gathered KV rows count 2 * d_qk bytes per valid slot
+    (the pages' model); partials are fp32 per valid slot."""
+    T, H, dqk, dv, S, W = p.T, p.H, p.d_qk, p.d_v, p.S_kv, p.W
+    return {
+        "fwd": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2),
+        "preprocess": (0.0, 2 * T * H * dv * 2 + T * H * 4),
+        "index_inversion": (0.0, 2 * T * W * 4 + n * 4),
+        "sdp": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2 + 2 * H * n * 2),
+        "dq": (2.0 * H * dqk * n, n * dqk * 2 + H * n * 2 + T * H * dqk * 2),
+        "dkv": (2.0 * H * (dqk + dv) * n, 2 * H * n * 2 + T * H * (dqk + dv) * 2 + n * dqk * 4),
+        "dkv_reduce": (0.0, n * dqk * 4 + n * 4 + S * dqk * 4),
+        "dsink": (0.0, 2 * T * H * 4),
+    }
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_top_attention_topk_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the stage's kernel(s) from the committed counter
+    profile (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_dsv4_flash_h128.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    frag = STAGE_KERNEL[stage]
+    vals = [k["bytes_per_launch"] for name, k in rec["kernels"].items() if frag in name]
+    return int(sum(vals)) if vals else None
+
+
+def roofline_for(stage, seconds, work):
+    flop, nbytes = work
+    t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        achieved, peak, unit, bound = flop / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    return {
+        "kernel": stage, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+        "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(stage),
+        "avg_launch_us": round(seconds * 1e6, 1), "algorithmic_flop": flop,
+        "algorithmic_bytes": int(nbytes),
+    }
 
 
 def cpu_baseline(p, n_tokens):

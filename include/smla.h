@@ -122,6 +122,25 @@ smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const
                      float* dkv, float* d_sink, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Number of stages smla_bwd runs, in order: index inversion, S/P/dP/dS,
+ * dQ, per-slot dKV contributions, dKV row reduce, d_sink. */
+#define SMLA_BWD_STAGES 6
+
+/* smla_bwd with stage timing, for benchmarks and profilers.  Computes exactly
+ * what smla_bwd computes (same passages, same kernels) and in addition records
+ * stage_events[0] on `stream` before the first stage and stage_events[i] after
+ * stage i (i = 1..SMLA_BWD_STAGES).  stage_events: n_events >= 
+ * SMLA_BWD_STAGES + 1 hipEvent_t handles created by the caller (recorded, not
+ * created or destroyed, by the library).  Errors: SMLA_ERR_NULL for a NULL
+ * array or handle, SMLA_ERR_SHAPE if n_events is too small, then as smla_bwd.
+ */
+smla_status smla_bwd_profiled(const smla_dims* dims, const void* q, const void* kv,
+                              const void* dO, const float* lse, const float* delta,
+                              const int32_t* topk_idxs, const int32_t* topk_length,
+                              const float* attn_sink, void* dq, float* dkv, float* d_sink,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              void* const* stage_events, int n_events);
+
 /* Static description of a status code. */
 const char* smla_status_string(smla_status status);
 

@@ -44,6 +44,10 @@ def _load():
     lib.smla_bwd.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
                              ctypes.c_size_t, P]
     lib.smla_bwd.restype = ctypes.c_int
+    lib.smla_bwd_profiled.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
+                                      ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_void_p),
+                                      ctypes.c_int]
+    lib.smla_bwd_profiled.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int]
     lib.smla_status_string.restype = ctypes.c_char_p
     return lib
@@ -52,7 +56,9 @@ def _load():
 LIB = _load()
 
 EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_workspace_size", "smla_bwd",
-            "smla_status_string")
+            "smla_bwd_profiled", "smla_status_string")
+
+BWD_STAGES = ("index_inversion", "sdp", "dq", "dkv", "dkv_reduce", "dsink")
 
 
 def _check(status: int, what: str):
@@ -144,8 +150,12 @@ def smla_bwd_workspace_size(T, S_kv, H, d_qk, d_v, W, scale=1.0) -> int:
 
 
 def smla_bwd(q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, scale, dq=None, dkv=None,
-             d_sink=None, workspace=None, stream=None):
-    """Backward; returns (dq bf16 [T,H,d_qk], dkv fp32 [S_kv,d_qk], d_sink fp32 [H] or None)."""
+             d_sink=None, workspace=None, stream=None, stage_events=None):
+    """Backward; returns (dq bf16 [T,H,d_qk], dkv fp32 [S_kv,d_qk], d_sink fp32 [H] or None).
+
+    With ``stage_events`` (len(BWD_STAGES) + 1 torch.cuda.Event objects that
+    have been recorded once), smla_bwd_profiled runs instead and records them
+    at the stage boundaries."""
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 3)
     _need(kv, "kv", torch.bfloat16, dev, 2)
@@ -171,8 +181,19 @@ def smla_bwd(q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, scale, dq
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev, 1)
-    _check(LIB.smla_bwd(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta),
-                        _ptr(topk_idxs), _ptr(topk_length), _ptr(attn_sink), _ptr(dq), _ptr(dkv),
-                        _ptr(d_sink), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                        _stream(dev, stream)), "smla_bwd")
+    args = (ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta),
+            _ptr(topk_idxs), _ptr(topk_length), _ptr(attn_sink), _ptr(dq), _ptr(dkv),
+            _ptr(d_sink), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+            _stream(dev, stream))
+    if stage_events is None:
+        _check(LIB.smla_bwd(*args), "smla_bwd")
+    else:
+        handles = (ctypes.c_void_p * len(stage_events))(
+            *[ctypes.c_void_p(e.cuda_event) for e in stage_events])
+        _check(LIB.smla_bwd_profiled(*args, handles, len(stage_events)), "smla_bwd_profiled")
     return dq, dkv, d_sink
+
+
+def smla_bwd_profiled(*args, stage_events, **kw):
+    """smla_bwd recording ``stage_events`` at its stage boundaries."""
+    return smla_bwd(*args, stage_events=stage_events, **kw)

@@ -113,10 +113,11 @@ size_t smla_bwd_workspace_size(const smla_dims* d) {
     return ws_layout(d).total;
 }
 
-smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const void* dO,
-                     const float* lse, const float* delta, const int32_t* topk_idxs,
-                     const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
-                     float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
+static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                            const float* lse, const float* delta, const int32_t* topk_idxs,
+                            const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
+                            float* d_sink, void* workspace, size_t workspace_bytes, void* stream,
+                            void* const* events) {
     smla_status st = check_dims(d);
     if (st != SMLA_OK) return st;
     if (!dkv) return SMLA_ERR_NULL;
@@ -154,8 +155,30 @@ smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const vo
     a.partial = reinterpret_cast<float*>(ws + WL.part);
     a.scale = d->scale;
     a.scale_log2 = d->scale * smla::LOG2E;
-    hipError_t e = smla::launch_bwd(d->d_qk, a, d_sink, static_cast<hipStream_t>(stream));
+    hipError_t e = smla::launch_bwd(d->d_qk, a, d_sink, static_cast<hipStream_t>(stream),
+                                    reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)));
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                     const float* lse, const float* delta, const int32_t* topk_idxs,
+                     const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
+                     float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(d, q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, dq, dkv, d_sink,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+smla_status smla_bwd_profiled(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                              const float* lse, const float* delta, const int32_t* topk_idxs,
+                              const int32_t* topk_length, const float* attn_sink, void* dq,
+                              float* dkv, float* d_sink, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* stage_events, int n_events) {
+    if (stage_events == nullptr) return SMLA_ERR_NULL;
+    if (n_events < SMLA_BWD_STAGES + 1) return SMLA_ERR_SHAPE;
+    for (int i = 0; i <= SMLA_BWD_STAGES; ++i)
+        if (stage_events[i] == nullptr) return SMLA_ERR_NULL;
+    return bwd_impl(d, q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, dq, dkv, d_sink,
+                    workspace, workspace_bytes, stream, stage_events);
 }
 
 }  // extern "C"

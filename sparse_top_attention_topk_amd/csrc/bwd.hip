@@ -685,25 +685,40 @@ static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int DQK>
-static void launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
+    auto mark = [&](int i) {
+        if (ev != nullptr) hipEventRecord(ev[i], stream);
+    };
     const int hk = (a.H + 31) / 32;
     if (a.H > 64) {
         hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 2>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        mark(2);
         hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.T, 1), dim3(512), 0, stream, a);
     } else {
         hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        mark(2);
         hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
     }
+    mark(3);
     switch (hk) {
         case 1: launch_dkv_t<DQK, 1>(a, stream); break;
         case 2: launch_dkv_t<DQK, 2>(a, stream); break;
         case 3: launch_dkv_t<DQK, 3>(a, stream); break;
         default: launch_dkv_t<DQK, 4>(a, stream); break;
     }
+    mark(4);
     hipLaunchKernelGGL((dkv_reduce_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
+    mark(5);
 }
 
-hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream) {
+hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream,
+                      hipEvent_t* ev) {
+    // stage boundaries: 0 start | 1 index inversion | 2 sdp | 3 dq | 4 dkv |
+    // 5 reduce | 6 d_sink
+    auto mark = [&](int i) {
+        if (ev != nullptr) hipEventRecord(ev[i], stream);
+    };
+    mark(0);
     if (a.T > 0) {
         const int nch = (a.T + a.tchunk - 1) / a.tchunk;
         const size_t lds = (size_t)a.S_kv * sizeof(int);
@@ -715,19 +730,23 @@ hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t str
         hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
         hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);
-        if (d_qk == 576) launch_bwd_t<576>(a, stream);
-        else launch_bwd_t<512>(a, stream);
+        mark(1);
+        if (d_qk == 576) launch_bwd_t<576>(a, stream, ev);
+        else launch_bwd_t<512>(a, stream, ev);
     } else {
         // no tokens: dkv is all zeros
+        mark(1);
         const size_t n = (size_t)a.S_kv * d_qk;
         const size_t want = (n + 255) / 256;
         const int fb = (int)(want < 4096 ? want : 4096);
         hipLaunchKernelGGL(fill_i32_kernel, dim3(fb), dim3(256), 0, stream,
                            reinterpret_cast<int*>(a.dkv), 0, n);
+        mark(2); mark(3); mark(4); mark(5);
     }
     if (a.sink != nullptr)
         hipLaunchKernelGGL(dsink_kernel, dim3(a.H), dim3(256), 0, stream, a.lse, a.delta, a.sink,
                            d_sink, a.T, a.H);
+    mark(6);
     return hipGetLastError();
 }
 

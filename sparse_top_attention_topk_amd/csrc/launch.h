@@ -45,6 +45,8 @@ struct BwdArgs {
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,
                              hipStream_t stream);
-hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream);
+// ev: NULL, or SMLA_BWD_STAGES + 1 events recorded at the stage boundaries
+hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream,
+                      hipEvent_t* ev);
 
 }  // namespace smla

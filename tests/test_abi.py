@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd",
-                                           "smla_bwd_workspace_size", "smla_status_string"])
+                                           "smla_bwd_workspace_size", "smla_bwd_profiled",
+                                           "smla_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -106,3 +107,15 @@ def test_workspace_size_and_check(lib):
     st = lib.LIB.smla_bwd(ctypes.byref(d), p, p, p, p, p, p, None, p, p, p, None, p,
                           ctypes.c_size_t(1 << 20), None)
     assert st == 1
+
+
+def test_profiled_rejects_missing_events(lib):
+    d = _dims(lib)
+    p = ctypes.c_void_p(0x1000)
+    args = [ctypes.byref(d), p, p, p, p, p, p, None, None, p, p, None, p,
+            ctypes.c_size_t(1 << 30), None]
+    assert lib.LIB.smla_bwd_profiled(*args, None, 7) == 1
+    evs = (ctypes.c_void_p * 7)(*([ctypes.c_void_p(0x10)] * 7))
+    assert lib.LIB.smla_bwd_profiled(*args, evs, 6) == 2
+    evs[3] = None
+    assert lib.LIB.smla_bwd_profiled(*args, evs, 7) == 1
