@@ -183,10 +183,11 @@ def main():
 
 
 # kernel-name fragment of each timed stage (for the counter profile)
-STAGE_KERNEL = {"fwd": "fwd_kernel", "preprocess": "preprocess_kernel",
-                "index_inversion": "rows_", "sdp": "bwd_sdp_kernel", "dq": "bwd_dq_kernel",
-                "dkv": "bwd_dkv_kernel", "dkv_reduce": "dkv_reduce_kernel",
-                "dsink": "dsink_kernel"}
+STAGE_KERNEL = {"fwd": ("fwd_kernel",), "preprocess": ("preprocess_kernel",),
+                "index_inversion": ("rows_",), "sdp": ("bwd_sdp_kernel",),
+                "dq": ("bwd_dq_kernel",), "dkv": ("bwd_dkv_kernel",),
+                "dkv_reduce": ("dkv_part_kernel", "dkv_combine_kernel"),
+                "dsink": ("dsink_kernel",)}
 
 
 def stage_work(p, n):
@@ -227,8 +228,9 @@ def measured_traffic(stage):
         return None
     if rec.get("source_sha256") != source_hash():
         return None
-    frag = STAGE_KERNEL[stage]
-    vals = [k["bytes_per_launch"] for name, k in rec["kernels"].items() if frag in name]
+    frags = STAGE_KERNEL[stage]
+    vals = [k["bytes_per_launch"] for name, k in rec["kernels"].items()
+            if any(f in name for f in frags)]
     return int(sum(vals)) if vals else None
 
 

@@ -23,8 +23,10 @@
 //   bwd_dkv      one workgroup per token: contracts over all heads,
 //                u = (scale dS)^T q + P^T dO per valid slot (fp32), written to
 //                the slot's row of a [T * Wp, d_qk] partial buffer
-//   dkv_reduce   one wave per KV row: sums the partial rows of the row's list
-//                in token order and writes dkv (unnamed rows get 0)
+//   dkv_part / dkv_combine
+//                sum each row's listed partials in token order, in bounded
+//                parts (one wave each) and then per row; write dkv (rows no
+//                valid slot names get 0)
 //   dsink        one workgroup per head: sum over tokens in token order
 // No fp32 atomics touch dkv: the scatter is a write of per-slot partials plus
 // a streaming reduce.  An empty row (no valid slot) is a uniform branch: dQ = 0
@@ -109,29 +111,55 @@ __global__ __launch_bounds__(256) void rows_chunkscan_kernel(BwdArgs a) {
     a.row_cnt[r] = run;
 }
 
-// Exclusive scan of the row totals into row_off[0..S_kv] (one workgroup).
+// Exclusive scans over the rows (one workgroup): row_off from the row totals,
+// and part_off from the number of reduce parts of each row (a row's list is
+// cut into parts of at most RPART entries, each summed by one wave).
+constexpr int RPART = 64;
+
+__device__ __forceinline__ int nparts(int cnt) { return (cnt + RPART - 1) / RPART; }
+
 __global__ __launch_bounds__(1024) void rows_scan_kernel(BwdArgs a) {
     __shared__ int s_part[1024];
+    __shared__ int s_part2[1024];
     const int n = a.S_kv;
     const int per = (n + 1023) / 1024;
     const int lo = (int)threadIdx.x * per < n ? (int)threadIdx.x * per : n;
     const int hi = lo + per < n ? lo + per : n;
-    int sum = 0;
-    for (int r = lo; r < hi; ++r) sum += a.row_cnt[r];
+    int sum = 0, sum2 = 0;
+    for (int r = lo; r < hi; ++r) {
+        sum += a.row_cnt[r];
+        sum2 += nparts(a.row_cnt[r]);
+    }
     s_part[threadIdx.x] = sum;
+    s_part2[threadIdx.x] = sum2;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
         const int v = (int)threadIdx.x >= d ? s_part[threadIdx.x - d] : 0;
+        const int v2 = (int)threadIdx.x >= d ? s_part2[threadIdx.x - d] : 0;
         __syncthreads();
         s_part[threadIdx.x] += v;
+        s_part2[threadIdx.x] += v2;
         __syncthreads();
     }
-    int run = s_part[threadIdx.x] - sum;     // exclusive prefix of this thread's rows
+    int run = s_part[threadIdx.x] - sum;     // exclusive prefixes of this thread's rows
+    int run2 = s_part2[threadIdx.x] - sum2;
     for (int r = lo; r < hi; ++r) {
         a.row_off[r] = run;
+        a.part_off[r] = run2;
         run += a.row_cnt[r];
+        run2 += nparts(a.row_cnt[r]);
     }
-    if (threadIdx.x == 1023) a.row_off[n] = s_part[1023];
+    if (threadIdx.x == 1023) {
+        a.row_off[n] = s_part[1023];
+        a.part_off[n] = s_part2[1023];
+    }
+}
+
+// part -> row map for the reduce
+__global__ __launch_bounds__(256) void rows_parts_kernel(BwdArgs a) {
+    const int r = (int)blockIdx.x * 256 + threadIdx.x;
+    if (r >= a.S_kv) return;
+    for (int p = a.part_off[r]; p < a.part_off[r + 1]; ++p) a.part_row[p] = r;
 }
 
 __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
@@ -602,44 +630,69 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dkv_reduce: dkv[r] = sum of the partial rows listed in r's segment, in list
-// (token) order.
-// One wave per KV row; lane l owns columns 4l..4l+3 (+256, +512 as needed).
+// dKV reduce, two levels, fixed order (so dkv is the same bits every run):
+//   dkv_part     one wave per part (<= RPART consecutive entries of one row's
+//                list): sums the listed partial rows in list (token) order
+//   dkv_combine  one wave per KV row: sums the row's parts in order and writes
+//                dkv (rows that no valid slot names get 0)
+// Cutting long lists into parts keeps every wave's work bounded: the first KV
+// rows are named by thousands of tokens, the last ones by a few.
+// Lane l owns columns 4l..4l+3 (+256, +512 as needed).
 // ---------------------------------------------------------------------------
 template <int DQK>
-__global__ __launch_bounds__(256) void dkv_reduce_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void dkv_part_kernel(BwdArgs a) {
     constexpr int NV = (DQK / 4 + 63) / 64;   // float4 per lane (3 for 576, 2 for 512)
-    const int r = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int U = 8;                       // partial rows in flight per wave
+    const int p = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (r >= a.S_kv) return;
-    const int lo = a.row_off[r], hi = a.row_off[r + 1];
+    if (p >= a.part_off[a.S_kv]) return;
+    const int r = a.part_row[p];
+    const int lo = a.row_off[r] + (p - a.part_off[r]) * RPART;
+    const int hi = lo + RPART < a.row_off[r + 1] ? lo + RPART : a.row_off[r + 1];
+    const int cnt = hi - lo;                   // 1..RPART
+    const int my_ent = lane < cnt ? a.entries[lo + lane] : 0;
     f32x4 acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = zero4();
-    int e = lo;
-    for (; e + 2 <= hi; e += 2) {
-        const float* p0 = a.partial + (size_t)a.entries[e] * DQK;
-        const float* p1 = a.partial + (size_t)a.entries[e + 1] * DQK;
-        f32x4 x0[NV], x1[NV];
+    for (int k0 = 0; k0 < cnt; k0 += U) {
+        f32x4 x[U][NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int c = 4 * (lane + 64 * v);
-            x0[v] = zero4();
-            x1[v] = zero4();
-            if (c < DQK) {
-                x0[v] = *reinterpret_cast<const f32x4*>(p0 + c);
-                x1[v] = *reinterpret_cast<const f32x4*>(p1 + c);
+        for (int u = 0; u < U; ++u) {
+            const int e = __shfl(my_ent, k0 + u, 64);
+            const float* src = a.partial + (size_t)e * DQK;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int c = 4 * (lane + 64 * v);
+                x[u][v] = (k0 + u < cnt && c < DQK) ? *reinterpret_cast<const f32x4*>(src + c) : zero4();
             }
         }
 #pragma unroll
-        for (int v = 0; v < NV; ++v) { acc[v] += x0[v]; acc[v] += x1[v]; }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v] += x[u][v];
     }
-    if (e < hi) {
-        const float* p0 = a.partial + (size_t)a.entries[e] * DQK;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int c = 4 * (lane + 64 * v);
+        if (c < DQK) *reinterpret_cast<f32x4*>(a.part_sum + (size_t)p * DQK + c) = acc[v];
+    }
+}
+
+template <int DQK>
+__global__ __launch_bounds__(256) void dkv_combine_kernel(BwdArgs a) {
+    constexpr int NV = (DQK / 4 + 63) / 64;
+    const int r = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= a.S_kv) return;
+    const int p0 = a.part_off[r], p1 = a.part_off[r + 1];
+    f32x4 acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = zero4();
+    for (int p = p0; p < p1; ++p) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int c = 4 * (lane + 64 * v);
-            if (c < DQK) acc[v] += *reinterpret_cast<const f32x4*>(p0 + c);
+            if (c < DQK) acc[v] += *reinterpret_cast<const f32x4*>(a.part_sum + (size_t)p * DQK + c);
         }
     }
 #pragma unroll
@@ -707,7 +760,8 @@ static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
         default: launch_dkv_t<DQK, 4>(a, stream); break;
     }
     mark(4);
-    hipLaunchKernelGGL((dkv_reduce_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dkv_part_kernel<DQK>), dim3((a.max_parts + 3) / 4), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dkv_combine_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
     mark(5);
 }
 
@@ -729,6 +783,7 @@ hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t str
         hipLaunchKernelGGL(rows_count_kernel, dim3(nch), dim3(256), lds, stream, a);
         hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(rows_parts_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);
         mark(1);
         if (d_qk == 576) launch_bwd_t<576>(a, stream, ev);

@@ -37,6 +37,10 @@ struct BwdArgs {
     int* row_off;     // [S_kv + 1]: segment starts of the row-grouped list
     int* entries;     // [T * W]: flat slot indices t * Wp + j, grouped by row
     float* partial;   // [T * Wp, d_qk] fp32: per-slot dKV contributions
+    int* part_off;    // [S_kv + 1]: first reduce part of each row
+    int* part_row;    // [max_parts]: row of each reduce part
+    float* part_sum;  // [max_parts, d_qk] fp32: sums of the parts
+    int max_parts;
     int T, S_kv, H, W, Wp;
     int tchunk;       // tokens per chunk of the index inversion
     float scale, scale_log2;

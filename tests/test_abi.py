@@ -91,7 +91,11 @@ def _ws_expected(T, S_kv, H, d_qk, W):
     off = a(off + S_kv * 4)              # row counts
     off = a(off + (S_kv + 1) * 4)        # row offsets
     off = a(off + T * W * 4)             # row lists
-    return a(off + T * Wp * d_qk * 4)    # partials
+    off = a(off + T * Wp * d_qk * 4)     # partials
+    mp = T * W // 64 + S_kv
+    off = a(off + (S_kv + 1) * 4)        # part offsets
+    off = a(off + mp * 4)                # part rows
+    return a(off + mp * d_qk * 4)        # part sums
 
 
 def test_workspace_size_and_check(lib):
