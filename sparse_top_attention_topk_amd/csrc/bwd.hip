@@ -195,19 +195,20 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
                                                 int (*s_rows)[BLK], int t, int L, int nblk,
                                                 int wave, int lane, Body&& body) {
     using Tile = KvTileSwz<DQK>;
+    const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
     if (tid < BLK) {
         s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
         s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
     }
     __syncthreads();
-    if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], a.kv, wave, lane);
+    if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         __syncthreads();
         int ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane);
+        if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
         body(s_tile0, s_rows[b % 3], b);
         if (b + 2 < nblk && tid < BLK)
             s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
@@ -216,7 +217,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane);
+        if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
         body(s_tile1, s_rows[(b + 1) % 3], b + 1);
         if (b + 3 < nblk && tid < BLK)
             s_rows[(b + 3) % 3][tid] = valid_row_b(ahead, (b + 3) * BLK + tid, L, a.S_kv);
@@ -344,13 +345,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // bwd_dq: dQ^T = K^T (scale dS)^T for all heads of one token.  NW waves; wave
 // w owns NT x 16 heads and 1/CS of the d_qk columns (CS column groups, the
-// waves of one head group are adjacent).
+// waves of one head group are adjacent): 32/CS main column tiles starting at a
+// multiple of 16 tiles, plus (d_qk = 576) 4/CS of the rope column tiles.
 // ---------------------------------------------------------------------------
 template <int DQK, int NW, int NT, int CS>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     using Tile = KvTileSwz<DQK>;
-    constexpr int MCW = DQK / 16 / CS;                 // column tiles per wave
-    constexpr int HT = NW / CS * NT * 16;              // heads per workgroup
+    constexpr int MAIN_PER = Tile::MC_MAIN / CS;               // main column tiles per wave
+    constexpr int ROPE_PER = Tile::ROPE ? 4 / CS : 0;          // rope column tiles per wave
+    constexpr int MCW = MAIN_PER + ROPE_PER;
+    constexpr int HT = NW / CS * NT * 16;                      // heads per workgroup
+    static_assert(MAIN_PER % 8 == 0, "main tile groups must keep mc % 8 static");
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
@@ -361,7 +366,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     const int g = lane >> 4, n = lane & 15;
     const int t = a.T - 1 - (int)blockIdx.x;
     const int h_wave = (int)blockIdx.y * HT + (wave / CS) * NT * 16;
-    const int mc0 = (wave % CS) * MCW;
+    const int cgrp = wave % CS;
+    const int mcb = cgrp * MAIN_PER;                           // first main tile
+    const int rpb = cgrp * ROPE_PER;                           // first rope tile
     const bool active = h_wave < a.H;
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
@@ -372,6 +379,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mc][nt] = zero4();
     const typename Tile::Lane TL = Tile::lane_bases(lane);
+
+    // K^T operands of the wave's column tile k (slots 0..31 and 32..63)
+    auto kload = [&](const __bf16* tile, int k, bf16x8 (&dst)[2]) {
+        if (k < MAIN_PER) {
+            dst[0] = Tile::slot_op_main(tile, TL, 0, mcb + k);
+            dst[1] = Tile::slot_op_main(tile, TL, 32, mcb + k);
+        } else {
+            dst[0] = Tile::slot_op_rope(tile, TL, 0, rpb + k - MAIN_PER);
+            dst[1] = Tile::slot_op_rope(tile, TL, 32, rpb + k - MAIN_PER);
+        }
+    };
 
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
                              [&](const __bf16* tile, const int* rows, int b) {
@@ -397,15 +415,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
             }
         }
         bf16x8 kop[2][2];
-        kop[0][0] = Tile::slot_op(tile, TL, 0, mc0);
-        kop[0][1] = Tile::slot_op(tile, TL, 32, mc0);
+        kload(tile, 0, kop[0]);
 #pragma unroll
         for (int mc = 0; mc < MCW; ++mc) {
             const int cur = mc & 1;
-            if (mc + 1 < MCW) {
-                kop[cur ^ 1][0] = Tile::slot_op(tile, TL, 0, mc0 + mc + 1);
-                kop[cur ^ 1][1] = Tile::slot_op(tile, TL, 32, mc0 + mc + 1);
-            }
+            if (mc + 1 < MCW) kload(tile, mc + 1, kop[cur ^ 1]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 acc[mc][nt] = mfma16(kop[cur][0], dsop[0][nt], acc[mc][nt]);
@@ -420,10 +434,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
         const int head = h_wave + nt * 16 + n;
         if (head >= a.H) continue;
-        __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 16 * mc0 + 4 * g;
+        __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 4 * g;
 #pragma unroll
-        for (int mc = 0; mc < MCW; ++mc)
-            st4(dqp + mc * 16, cvt4(acc[mc][nt][0], acc[mc][nt][1], acc[mc][nt][2], acc[mc][nt][3]));
+        for (int mc = 0; mc < MCW; ++mc) {
+            const int col = mc < MAIN_PER ? 16 * (mcb + mc) : 16 * (Tile::MC_MAIN + rpb + mc - MAIN_PER);
+            st4(dqp + col, cvt4(acc[mc][nt][0], acc[mc][nt][1], acc[mc][nt][2], acc[mc][nt][3]));
+        }
     }
 }
 
@@ -446,6 +462,21 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // conflicts.
 __device__ __forceinline__ int pf(int h) { return (((h >> 1) & 1) << 1) | (((h >> 3) & 1) << 2); }
 
+// Chunk permutation of the staged q / dO rows: stage_op reads rows
+// {8g + i, 8g + 4 + i}, and each 32-lane pass of its transposed reads must
+// see 8 rows on distinct banks (1152-byte rows alternate between two bank
+// halves by themselves; 1024-byte rows all start at bank 0).
+template <int D>
+struct StageF;
+template <>
+struct StageF<576> {
+    __device__ static int f(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2); }
+};
+template <>
+struct StageF<512> {
+    __device__ static int f(int r) { return ((r & 3) << 1) | (((r >> 3) & 1) << 3); }
+};
+
 template <int D, int NW>
 __device__ __forceinline__ void stage_rows_async(__bf16* dst, const __bf16* src_rows, int nrows_valid,
                                                  int wave_s, int lane) {
@@ -462,7 +493,7 @@ __device__ __forceinline__ void stage_rows_async(__bf16* dst, const __bf16* src_
         const int row = pos / CH;
         const int pc = pos - row * CH;
         const int rr = row < nrows_valid ? row : nrows_valid - 1;
-        const __bf16* src = src_rows + (size_t)rr * D + ((pc ^ SwzF<D>::f(row)) << 3);
+        const __bf16* src = src_rows + (size_t)rr * D + ((pc ^ StageF<D>::f(row)) << 3);
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + i * 512), 16, 0, 0);
     }
 }
@@ -474,8 +505,8 @@ __device__ __forceinline__ bf16x8 stage_op(const __bf16* stage, int c0, int lane
     const int g = lane >> 4, w = lane & 15;
     const int row = 8 * g + (w >> 2);
     const int col = c0 + 4 * (w & 3);
-    const int e0 = row * D + ((((col >> 3) ^ SwzF<D>::f(row))) << 3) + (col & 7);
-    const int e1 = (row + 4) * D + ((((col >> 3) ^ SwzF<D>::f(row + 4))) << 3) + (col & 7);
+    const int e0 = row * D + ((((col >> 3) ^ StageF<D>::f(row))) << 3) + (col & 7);
+    const int e1 = (row + 4) * D + ((((col >> 3) ^ StageF<D>::f(row + 4))) << 3) + (col & 7);
     return cat44(lds_tr4(stage + e0), lds_tr4(stage + e1));
 }
 

@@ -196,6 +196,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         for (int ks = 0; ks < C::KS; ++ks) qop[nt][ks] = hv ? ld8(qp + 32 * ks) : zero8();
     }
     const typename Tile::Lane TL = Tile::lane_bases(lane);
+    const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     f32x4 oacc[C::MC][NT];
     float m_ref[NT], rmax[NT], l_run[NT], l_rnd[NT];
 #pragma unroll
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
         }
         __syncthreads();
-        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], a.kv, wave, lane);
+        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
 
         // Two blocks per iteration so that each tile is a distinct LDS object.
         // Per block: wait for this block's tile, start the next block's
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __syncthreads();
             int ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
-            if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane);
+            if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
             if (active) fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
             if (b + 2 < nblk && tid < BLK)
                 s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __syncthreads();
             ahead = tid < BLK ? raw_index(a, t, (b + 3) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
-            if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane);
+            if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
             if (active) fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
             if (b + 3 < nblk && tid < BLK)
                 s_rows[(b + 3) % 3][tid] = valid_row(ahead, (b + 3) * BLK + tid, L, a.S_kv);
