@@ -34,6 +34,8 @@
 #include "kv_tile.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace smla {
 
 // ---------------------------------------------------------------------------
@@ -188,13 +190,23 @@ __device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
 }
 
 // The double-buffered gather loop of the kernels that gather KV tiles:
-// body(tile, rows, b) runs block b from tile 0 (even b) or tile 1 (odd b)
-// while the next block's rows are in flight into the other tile.
-template <int DQK, int NW, typename Body>
+// body(tile, rows, b, parity) runs block b from tile 0 (even b, parity 0) or
+// tile 1 (odd b, parity 1) while the next block's rows are in flight into the
+// other tile.  pre(b, parity) runs before the gather of block b is issued and
+// may issue global loads for block b (they complete before block b starts,
+// and waiting for them never waits for a gather issued after them).
+struct NoPre {
+    template <typename P>
+    __device__ void operator()(int, P) const {}
+};
+
+template <int DQK, int NW, typename Body, typename Pre = NoPre>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
                                                 int (*s_rows)[BLK], int t, int L, int nblk,
-                                                int wave, int lane, Body&& body) {
+                                                int wave, int lane, Body&& body, Pre&& pre = Pre{}) {
     using Tile = KvTileSwz<DQK>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
     if (tid < BLK) {
@@ -202,14 +214,20 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
     }
     __syncthreads();
-    if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+    if (nblk > 0) {
+        pre(0, P0{});
+        Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+    }
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         __syncthreads();
         int ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
-        body(s_tile0, s_rows[b % 3], b);
+        if (b + 1 < nblk) {
+            pre(b + 1, P1{});
+            Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
+        }
+        body(s_tile0, s_rows[b % 3], b, P0{});
         if (b + 2 < nblk && tid < BLK)
             s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
         if (b + 1 >= nblk) break;
@@ -217,8 +235,11 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
-        body(s_tile1, s_rows[(b + 1) % 3], b + 1);
+        if (b + 2 < nblk) {
+            pre(b + 2, P0{});
+            Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
+        }
+        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{});
         if (b + 3 < nblk && tid < BLK)
             s_rows[(b + 3) % 3][tid] = valid_row_b(ahead, (b + 3) * BLK + tid, L, a.S_kv);
     }
@@ -335,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
     }
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b) {
+                             [&](const __bf16* tile, const int* rows, int b, auto) {
                                  if (active)
                                      sdp_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, dlt, t,
                                                             h_wave, b, lane);
@@ -391,13 +412,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b) {
-        (void)rows;
+    // (scale dS)^T as B operands: lane (g, n) holds 8 slots of head n in the
+    // slot order of slot_op: 32kk + 4g + j (j < 4), 32kk + 16 + 4g + j - 4.
+    // Loaded one block ahead (before that block's gather is issued) into the
+    // buffer of the block's parity.
+    bf16x8 dsop[2][2][NT];
+    auto load_ds = [&](int b, auto par) {
         if (!active) return;
-        // (scale dS)^T as B operands: lane (g, n) holds 8 slots of head n in
-        // the slot order of slot_op: 32kk + 4g + j (j < 4), 32kk + 16 + 4g + j - 4
-        bf16x8 dsop[2][NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int head = h_wave + nt * 16 + n;
@@ -408,12 +429,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 if (hv) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 32 * kk);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 32 * kk + 16);
-                    dsop[kk][nt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    dsop[par][kk][nt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                 } else {
-                    dsop[kk][nt] = zero8();
+                    dsop[par][kk][nt] = zero8();
                 }
             }
         }
+    };
+
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
+                             [&](const __bf16* tile, const int* rows, int b, auto par) {
+        (void)rows;
+        (void)b;
+        if (!active) return;
         bf16x8 kop[2][2];
         kload(tile, 0, kop[0]);
 #pragma unroll
@@ -422,12 +450,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
             if (mc + 1 < MCW) kload(tile, mc + 1, kop[cur ^ 1]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                acc[mc][nt] = mfma16(kop[cur][0], dsop[0][nt], acc[mc][nt]);
-                acc[mc][nt] = mfma16(kop[cur][1], dsop[1][nt], acc[mc][nt]);
+                acc[mc][nt] = mfma16(kop[cur][0], dsop[par][0][nt], acc[mc][nt]);
+                acc[mc][nt] = mfma16(kop[cur][1], dsop[par][1][nt], acc[mc][nt]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    });
+    }, load_ds);
 
     if (!active) return;
 #pragma unroll
