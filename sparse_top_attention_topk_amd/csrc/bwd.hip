@@ -802,8 +802,11 @@ static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
         if (ev != nullptr) hipEventRecord(ev[i], stream);
     };
     const int hk = (a.H + 31) / 32;
+    // sdp: 16 heads per wave keep q and dO (the B operands) within half the
+    // register file, so two waves share each SIMD and hide each other's
+    // gather and LDS latency; 8 such waves cover 128 heads.
     if (a.H > 64) {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 2>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.T, 1), dim3(512), 0, stream, a);
         mark(2);
         hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.T, 1), dim3(512), 0, stream, a);
     } else {
