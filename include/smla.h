@@ -106,9 +106,12 @@ size_t smla_bwd_workspace_size(const smla_dims* dims);
  *              valid slot (that token's q, dO, lse and delta are not read)
  *   dkv        fp32 [S_kv, d_qk] out: row r is the sum, over the valid slots
  *              that name r taken in token order, of scale * dS^T q (all d_qk
- *              columns) plus P^T dO (first d_v columns); the order is fixed,
- *              so dkv is the same bits run to run.  Rows never named by a
- *              valid slot (e.g. row 0 for -1 sentinels) are exactly 0.
+ *              columns) plus P^T dO (first d_v columns); each slot's
+ *              contribution is accumulated in fp32 and kept with 16 bits of
+ *              significand (relative rounding <= 2^-16) until the row sum.
+ *              The order is fixed, so dkv is the same bits run to run.  Rows
+ *              never named by a valid slot (e.g. row 0 for -1 sentinels) are
+ *              exactly 0.
  *   d_sink     fp32 [H] out: -sum_t p_sink[t,h] * delta[t,h] with
  *              p_sink = sigmoid(sink - lse); required iff attn_sink != NULL
  * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16

@@ -21,8 +21,12 @@
 //   bwd_dq       one workgroup per token: gathers the KV tiles again and
 //                accumulates dQ^T = K^T (scale dS)^T in registers
 //   bwd_dkv      one workgroup per token: contracts over all heads,
-//                u = (scale dS)^T q + P^T dO per valid slot (fp32), written to
-//                the slot's row of a [T * Wp, d_qk] partial buffer
+//                u = (scale dS)^T q + P^T dO per valid slot (fp32 accumulate),
+//                written to the slot's row of a [T * Wp] partial buffer as
+//                24-bit values (fp32 rounded to nearest even at bit 8, so
+//                relative error <= 2^-16 per value; the row sums that follow
+//                add fp32 rounding of the same order, and the partial traffic,
+//                which bounds this half of the backward, drops by a quarter)
 //   dkv_part / dkv_combine
 //                sum each row's listed partials in token order, in bounded
 //                parts (one wave each) and then per row; write dkv (rows no
@@ -480,8 +484,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // per token through LDS with asynchronous loads (two buffers in flight).  The
 // P / dS tiles of the next block load asynchronously while the current block
 // is computed.  Each lane ends up holding 4 consecutive columns of u for one
-// slot and writes them as one 16-byte store into the slot's row of the
-// [T * Wp, d_qk] partial buffer.
+// slot and writes them as one 12-byte store (four 24-bit values) into the
+// slot's row of the partial buffer; slots that are not valid are skipped.
 // ---------------------------------------------------------------------------
 
 // P or scale*dS tile: [HP heads][64 slots] bf16, 128-byte rows, chunk c of row
@@ -570,9 +574,9 @@ __device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int 
 }
 
 template <int DQK, int HK>
-__device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd,
+__device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, const int* raw,
                                           const bf16x8 (&qB)[HK][DQK / 64],
-                                          const bf16x8 (&dB)[HK][DQK / 64], int t, int b,
+                                          const bf16x8 (&dB)[HK][DQK / 64], int t, int b, int L,
                                           int c_wave, int lane) {
     constexpr int DV = 512;
     constexpr int NTC = DQK / 64;
@@ -602,14 +606,19 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd,
             __builtin_amdgcn_sched_barrier(0);
         }
         // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot
-        // 32 half + 16 m + n; every slot of the block is written (invalid slots
-        // carry P = dS = 0, so u = 0, and the row lists never name them)
+        // 32 half + 16 m + n, stored as 24-bit values (12 bytes); only valid
+        // slots are written (the row lists name no other slot)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int slot = (2 * half + m) * 16 + n;
-            float* dst = a.partial + ((size_t)t * a.Wp + b * BLK + slot) * DQK + c_wave + 4 * g;
+            const int v = raw[slot];
+            if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
+                char* dst = reinterpret_cast<char*>(a.partial) +
+                            ((size_t)t * a.Wp + b * BLK + slot) * (3 * DQK) + 3 * (c_wave + 4 * g);
 #pragma unroll
-            for (int nt = 0; nt < NTC; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt) = acc[nt][m];
+                for (int nt = 0; nt < NTC; ++nt)
+                    *reinterpret_cast<u32x3*>(dst + 48 * nt) = pack24x4(acc[nt][m]);
+            }
         }
     }
 }
@@ -625,6 +634,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_st1[32 * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 s_pd0[2 * HP * BLK];   // [P | dS], even blocks
     __shared__ __attribute__((aligned(16))) __bf16 s_pd1[2 * HP * BLK];   // [P | dS], odd blocks
+    __shared__ int s_raw[2][BLK];                                          // raw top-k indices
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -663,8 +673,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
         __bf16* nxt = (piece & 1) ? s_st0 : s_st1;
         wait_vmem();
         __syncthreads();
-        if (piece + 1 < 2 * HK) issue(piece + 1, nxt);
-        else pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
+        if (piece + 1 < 2 * HK) {
+            issue(piece + 1, nxt);
+        } else {
+            pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
+            if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, 0, lane);
+        }
         const int hk = piece >> 1;
 #pragma unroll
         for (int nt = 0; nt < NTC; ++nt) {
@@ -678,13 +692,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         __syncthreads();
-        if (b + 1 < nblk) pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
-        dkv_block<DQK, HK>(a, s_pd0, qB, dB, t, b, c_wave, lane);
+        if (b + 1 < nblk) {
+            pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
+            if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
+        }
+        dkv_block<DQK, HK>(a, s_pd0, s_raw[0], qB, dB, t, b, L, c_wave, lane);
         if (b + 1 >= nblk) break;
         wait_vmem();
         __syncthreads();
-        if (b + 2 < nblk) pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
-        dkv_block<DQK, HK>(a, s_pd1, qB, dB, t, b + 1, c_wave, lane);
+        if (b + 2 < nblk) {
+            pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
+            if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
+        }
+        dkv_block<DQK, HK>(a, s_pd1, s_raw[1], qB, dB, t, b + 1, L, c_wave, lane);
     }
 }
 
@@ -700,8 +720,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <int DQK>
 __global__ __launch_bounds__(256) void dkv_part_kernel(BwdArgs a) {
-    constexpr int NV = (DQK / 4 + 63) / 64;   // float4 per lane (3 for 576, 2 for 512)
-    constexpr int U = 8;                       // partial rows in flight per wave
+    // lane l < DQK / 16 owns columns 16 l .. 16 l + 15: 48 packed bytes, three
+    // 16-byte loads per row
+    constexpr int G = DQK / 16;
+    constexpr int U = 4;                       // partial rows in flight per wave
     const int p = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (p >= a.part_off[a.S_kv]) return;
@@ -710,30 +732,32 @@ __global__ __launch_bounds__(256) void dkv_part_kernel(BwdArgs a) {
     const int hi = lo + RPART < a.row_off[r + 1] ? lo + RPART : a.row_off[r + 1];
     const int cnt = hi - lo;                   // 1..RPART
     const int my_ent = lane < cnt ? a.entries[lo + lane] : 0;
-    f32x4 acc[NV];
+    const bool act = lane < G;
+    f32x4 acc[4];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = zero4();
+    for (int v = 0; v < 4; ++v) acc[v] = zero4();
     for (int k0 = 0; k0 < cnt; k0 += U) {
-        f32x4 x[U][NV];
+        u32x4 x[U][3];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = __shfl(my_ent, k0 + u, 64);
-            const float* src = a.partial + (size_t)e * DQK;
+            const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.partial) +
+                                                              (size_t)e * (3 * DQK) + 48 * lane);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int c = 4 * (lane + 64 * v);
-                x[u][v] = (k0 + u < cnt && c < DQK) ? *reinterpret_cast<const f32x4*>(src + c) : zero4();
-            }
+            for (int v = 0; v < 3; ++v) x[u][v] = (k0 + u < cnt && act) ? src[v] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int v = 0; v < NV; ++v) acc[v] += x[u][v];
+        for (int u = 0; u < U; ++u) {
+            acc[0] += unpack24x4(u32x3{x[u][0][0], x[u][0][1], x[u][0][2]});
+            acc[1] += unpack24x4(u32x3{x[u][0][3], x[u][1][0], x[u][1][1]});
+            acc[2] += unpack24x4(u32x3{x[u][1][2], x[u][1][3], x[u][2][0]});
+            acc[3] += unpack24x4(u32x3{x[u][2][1], x[u][2][2], x[u][2][3]});
+        }
     }
+    if (act) {
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const int c = 4 * (lane + 64 * v);
-        if (c < DQK) *reinterpret_cast<f32x4*>(a.part_sum + (size_t)p * DQK + c) = acc[v];
+        for (int v = 0; v < 4; ++v)
+            *reinterpret_cast<f32x4*>(a.part_sum + (size_t)p * DQK + 16 * lane + 4 * v) = acc[v];
     }
 }
 

@@ -21,6 +21,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) __bf16 lds_bf16;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -93,6 +94,40 @@ __device__ __forceinline__ int slot_row(const int32_t* idx, int t, int W, int L,
     if (j >= L) return -1;
     int v = idx[(size_t)t * W + j];
     return (v >= 0 && v < S_kv) ? v : -1;
+}
+
+// Stage the raw top-k indices of slots 64 b .. 64 b + 63 of token t into dst
+// (LDS) with one buffer load that writes LDS directly (a whole wave calls it;
+// slots past the end of the row read 0).  It completes with the caller's
+// vector-memory count.  A slot's validity is decided where it is used.
+__device__ __forceinline__ void stage_slot_idx(int* dst, const int32_t* idx, int t, int W, int b,
+                                               int lane) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(idx + (size_t)t * W), (short)0, W * 4, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (b * 64 + lane) * 4, 0, 0, 0);
+}
+
+// 24-bit storage of fp32 values (the dKV partials): the top 24 bits of the
+// fp32 pattern, rounded to nearest even on the 8 dropped bits, so a stored
+// value keeps sign, exponent and 15 mantissa bits (relative error <= 2^-16).
+// Four values pack into three dwords.
+__device__ __forceinline__ uint32_t f32_to_24(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+
+__device__ __forceinline__ u32x3 pack24x4(f32x4 v) {
+    const uint32_t r0 = f32_to_24(v[0]), r1 = f32_to_24(v[1]), r2 = f32_to_24(v[2]), r3 = f32_to_24(v[3]);
+    return u32x3{r0 | (r1 << 24), (r1 >> 8) | (r2 << 16), (r2 >> 16) | (r3 << 8)};
+}
+
+__device__ __forceinline__ f32x4 unpack24x4(u32x3 w) {
+    const uint32_t r0 = w[0] & 0xFFFFFFu;
+    const uint32_t r1 = (w[0] >> 24) | ((w[1] & 0xFFFFu) << 8);
+    const uint32_t r2 = (w[1] >> 16) | ((w[2] & 0xFFu) << 16);
+    const uint32_t r3 = w[2] >> 8;
+    return f32x4{__builtin_bit_cast(float, r0 << 8), __builtin_bit_cast(float, r1 << 8),
+                 __builtin_bit_cast(float, r2 << 8), __builtin_bit_cast(float, r3 << 8)};
 }
 
 // Finite-max-guarded logaddexp: ln(e^a + e^b); an infinite maximum is returned
