@@ -578,7 +578,6 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
                                           const bf16x8 (&qB)[HK][DQK / 64],
                                           const bf16x8 (&dB)[HK][DQK / 64], int t, int b, int L,
                                           int c_wave, int lane) {
-    constexpr int DV = 512;
     constexpr int NTC = DQK / 64;
     constexpr int HP = 32 * HK;
     const int g = lane >> 4, n = lane & 15;
@@ -599,8 +598,10 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
             for (int nt = 0; nt < NTC; ++nt) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
+                    // dB is zero for columns past d_v: unconditional, so the
+                    // MFMAs stay in one basic block for the scheduler
                     acc[nt][m] = mfma16(qB[hk][nt], bds[m], acc[nt][m]);
-                    if (c_wave + 16 * nt < DV) acc[nt][m] = mfma16(dB[hk][nt], bp[m], acc[nt][m]);
+                    acc[nt][m] = mfma16(dB[hk][nt], bp[m], acc[nt][m]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -821,9 +822,11 @@ static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
 }
 
 template <int DQK>
-static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev) {
+static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev, hipError_t& err) {
     auto mark = [&](int i) {
-        if (ev != nullptr) hipEventRecord(ev[i], stream);
+        if (ev == nullptr) return;
+        const hipError_t e = hipEventRecord(ev[i], stream);
+        if (err == hipSuccess) err = e;
     };
     const int hk = (a.H + 31) / 32;
     // sdp: 16 heads per wave keep q and dO (the B operands) within half the
@@ -855,25 +858,30 @@ hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t str
                       hipEvent_t* ev) {
     // stage boundaries: 0 start | 1 index inversion | 2 sdp | 3 dq | 4 dkv |
     // 5 reduce | 6 d_sink
+    hipError_t err = hipSuccess;
     auto mark = [&](int i) {
-        if (ev != nullptr) hipEventRecord(ev[i], stream);
+        if (ev == nullptr) return;
+        const hipError_t e = hipEventRecord(ev[i], stream);
+        if (err == hipSuccess) err = e;
     };
     mark(0);
     if (a.T > 0) {
         const int nch = (a.T + a.tchunk - 1) / a.tchunk;
         const size_t lds = (size_t)a.S_kv * sizeof(int);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipFuncSetAttribute(reinterpret_cast<const void*>(rows_fill_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err == hipSuccess)
+            err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_fill_kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
         hipLaunchKernelGGL(rows_count_kernel, dim3(nch), dim3(256), lds, stream, a);
         hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
         hipLaunchKernelGGL(rows_parts_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);
         mark(1);
-        if (d_qk == 576) launch_bwd_t<576>(a, stream, ev);
-        else launch_bwd_t<512>(a, stream, ev);
+        if (d_qk == 576) launch_bwd_t<576>(a, stream, ev, err);
+        else launch_bwd_t<512>(a, stream, ev, err);
     } else {
         // no tokens: dkv is all zeros
         mark(1);
@@ -888,7 +896,8 @@ hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t str
         hipLaunchKernelGGL(dsink_kernel, dim3(a.H), dim3(256), 0, stream, a.lse, a.delta, a.sink,
                            d_sink, a.T, a.H);
     mark(6);
-    return hipGetLastError();
+    const hipError_t le = hipGetLastError();
+    return le != hipSuccess ? le : err;
 }
 
 }  // namespace smla
