@@ -479,7 +479,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // bwd_dkv: per token and 64-slot block,
 //   u[slot][c] = sum_h (scale dS)[h][slot] q[h][c] + P[h][slot] dO[h][c]
 // computed as u^T = q^T (scale dS) + dO^T P, a contraction over heads (HK
-// k-steps of 32 heads).  Wave w owns the columns [w * DQK/4, (w+1) * DQK/4);
+// k-steps of 32 heads).  Eight waves (two per SIMD, so one wave's stores
+// overlap the other's MFMAs) split the 16-column tiles of d_qk: 5 or 4 each
+// for d_qk = 576, 4 each for 512.
 // q and dO for those columns stay in registers with heads in-lane, staged once
 // per token through LDS with asynchronous loads (two buffers in flight).  The
 // P / dS tiles of the next block load asynchronously while the current block
@@ -515,12 +517,12 @@ __device__ __forceinline__ void stage_rows_async(__bf16* dst, const __bf16* src_
     // 32 rows x D columns; rows >= nrows_valid repeat the last valid row
     constexpr int CH = D / 8;
     constexpr int INSTR = 32 * CH / 64;
-    static_assert(INSTR % NW == 0, "pieces must split evenly over the waves");
     int lv;
     asm volatile("v_mov_b32 %0, %1" : "=v"(lv) : "v"(lane));
 #pragma unroll
-    for (int k = 0; k < INSTR / NW; ++k) {
+    for (int k = 0; k < (INSTR + NW - 1) / NW; ++k) {
         const int i = k * NW + wave_s;
+        if (INSTR % NW != 0 && i >= INSTR) break;     // wave-uniform
         const int pos = i * 64 + lv;
         const int row = pos / CH;
         const int pc = pos - row * CH;
@@ -573,64 +575,55 @@ __device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int 
     return cat44(lds_tr4(tile + e0), lds_tr4(tile + e1));
 }
 
-template <int DQK, int HK>
+template <int DQK, int HK, int NTC>
 __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, const int* raw,
-                                          const bf16x8 (&qB)[HK][DQK / 64],
-                                          const bf16x8 (&dB)[HK][DQK / 64], int t, int b, int L,
-                                          int c_wave, int lane) {
-    constexpr int NTC = DQK / 64;
+                                          const bf16x8 (&qB)[HK][NTC],
+                                          const bf16x8 (&dB)[HK][NTC], int t, int b, int L,
+                                          int c_wave, int ntc, int lane) {
     constexpr int HP = 32 * HK;
     const int g = lane >> 4, n = lane & 15;
+    // four quarters of 16 slots: one accumulator tile per column tile
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        f32x4 acc[NTC][2];
+    for (int qt = 0; qt < 4; ++qt) {
+        f32x4 acc[NTC];
 #pragma unroll
-        for (int nt = 0; nt < NTC; ++nt) { acc[nt][0] = zero4(); acc[nt][1] = zero4(); }
+        for (int nt = 0; nt < NTC; ++nt) acc[nt] = zero4();
 #pragma unroll
         for (int hk = 0; hk < HK; ++hk) {
-            bf16x8 bds[2], bp[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                bp[m] = pd_op(pd, 32 * hk, (2 * half + m) * 16, lane);
-                bds[m] = pd_op(pd + HP * BLK, 32 * hk, (2 * half + m) * 16, lane);
-            }
+            const bf16x8 bp = pd_op(pd, 32 * hk, 16 * qt, lane);
+            const bf16x8 bds = pd_op(pd + HP * BLK, 32 * hk, 16 * qt, lane);
 #pragma unroll
             for (int nt = 0; nt < NTC; ++nt) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    // dB is zero for columns past d_v: unconditional, so the
-                    // MFMAs stay in one basic block for the scheduler
-                    acc[nt][m] = mfma16(qB[hk][nt], bds[m], acc[nt][m]);
-                    acc[nt][m] = mfma16(dB[hk][nt], bp[m], acc[nt][m]);
-                }
+                // dB is zero for columns past d_v: unconditional, so the MFMAs
+                // stay in one basic block for the scheduler
+                acc[nt] = mfma16(qB[hk][nt], bds, acc[nt]);
+                acc[nt] = mfma16(dB[hk][nt], bp, acc[nt]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
-        // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot
-        // 32 half + 16 m + n, stored as 24-bit values (12 bytes); only valid
-        // slots are written (the row lists name no other slot)
+        // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot 16 qt + n,
+        // stored as 24-bit values (12 bytes); only valid slots are written
+        // (the row lists name no other slot)
+        const int slot = 16 * qt + n;
+        const int v = raw[slot];
+        if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
+            char* dst = reinterpret_cast<char*>(a.partial) +
+                        ((size_t)t * a.Wp + b * BLK + slot) * (3 * DQK) + 3 * (c_wave + 4 * g);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int slot = (2 * half + m) * 16 + n;
-            const int v = raw[slot];
-            if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
-                char* dst = reinterpret_cast<char*>(a.partial) +
-                            ((size_t)t * a.Wp + b * BLK + slot) * (3 * DQK) + 3 * (c_wave + 4 * g);
-#pragma unroll
-                for (int nt = 0; nt < NTC; ++nt)
-                    *reinterpret_cast<u32x3*>(dst + 48 * nt) = pack24x4(acc[nt][m]);
-            }
+            for (int nt = 0; nt < NTC; ++nt)
+                if (NTC * 8 == DQK / 16 || nt < ntc)            // the wave's own tiles
+                    *reinterpret_cast<u32x3*>(dst + 48 * nt) = pack24x4(acc[nt]);
         }
     }
 }
 
 template <int DQK, int HK>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int DV = 512;
-    constexpr int NW = 4;
-    constexpr int CW = DQK / 4;          // columns per wave
-    constexpr int NTC = CW / 16;         // 16-column tiles per wave
-    constexpr int HP = 32 * HK;          // heads padded
+    constexpr int NW = 8;
+    constexpr int NTILES = DQK / 16;                    // 16-column tiles (36 or 32)
+    constexpr int NTC = (NTILES + NW - 1) / NW;         // tiles per wave, at most (5 or 4)
+    constexpr int R = NTILES - NW * (NTC - 1);          // waves that take NTC tiles
+    constexpr int HP = 32 * HK;                         // heads padded
     __shared__ __attribute__((aligned(16))) __bf16 s_st0[32 * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 s_st1[32 * DQK];
     __shared__ __attribute__((aligned(16))) __bf16 s_pd0[2 * HP * BLK];   // [P | dS], even blocks
@@ -644,11 +637,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
     if (nblk == 0) return;                 // uniform: an empty row adds nothing
-    const int c_wave = wave * CW;
+    // wave w owns tiles [tile0, tile0 + ntc): the first R waves NTC tiles, the
+    // rest NTC - 1 (their last tile slot is computed on zero operands and not
+    // stored)
+    const int tile0 = wave < R ? wave * NTC : R * NTC + (wave - R) * (NTC - 1);
+    const int ntc = wave < R ? NTC : NTC - 1;
+    const int c_wave = 16 * tile0;
 
     // heads past H: their P / dS tile rows stay zero (never loaded)
     if (HP > a.H) {
-        for (int i = tid; i < 2 * HP * BLK / 8; i += 256) {
+        for (int i = tid; i < 2 * HP * BLK / 8; i += NW * 64) {
             reinterpret_cast<u32x4*>(s_pd0)[i] = u32x4{0u, 0u, 0u, 0u};
             reinterpret_cast<u32x4*>(s_pd1)[i] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -684,8 +682,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NTC; ++nt) {
             const int c0 = c_wave + 16 * nt;
-            if ((piece & 1) == 0) qB[hk][nt] = stage_op<DQK>(cur, c0, lane);
-            else dB[hk][nt] = c0 < DV ? stage_op<DV>(cur, c0, lane) : zero8();
+            const bool own = nt < ntc;
+            if ((piece & 1) == 0) qB[hk][nt] = own ? stage_op<DQK>(cur, c0, lane) : zero8();
+            else dB[hk][nt] = own && c0 < DV ? stage_op<DV>(cur, c0, lane) : zero8();
         }
     }
 
@@ -697,7 +696,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
         }
-        dkv_block<DQK, HK>(a, s_pd0, s_raw[0], qB, dB, t, b, L, c_wave, lane);
+        dkv_block<DQK, HK, NTC>(a, s_pd0, s_raw[0], qB, dB, t, b, L, c_wave, ntc, lane);
         if (b + 1 >= nblk) break;
         wait_vmem();
         __syncthreads();
@@ -705,7 +704,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
         }
-        dkv_block<DQK, HK>(a, s_pd1, s_raw[1], qB, dB, t, b + 1, L, c_wave, lane);
+        dkv_block<DQK, HK, NTC>(a, s_pd1, s_raw[1], qB, dB, t, b + 1, L, c_wave, ntc, lane);
     }
 }
 
@@ -818,7 +817,7 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
 
 template <int DQK, int HK>
 static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.T), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.T), dim3(512), 0, stream, a);
 }
 
 template <int DQK>
