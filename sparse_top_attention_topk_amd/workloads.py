@@ -275,4 +275,7 @@ PROBLEMS = {
                                               name="dsv4_flash_h128_T4096", **kw),
     "dsv4_pro": lambda **kw: make_dsv4(16384, 128, 512, 512, 1024, seed=3,
                                        name="dsv4_pro_h128_T16384", **kw),
+    # the headline's index sets packed to the front with topk_length
+    "dsv4_flash_h128_compact": lambda **kw: make_dsv4(4096, 128, 576, 512, 512, seed=2, compact=True,
+                                                      name="dsv4_flash_h128_T4096_compact", **kw),
 }

@@ -107,7 +107,7 @@ def test_repeated_empty_and_mixed_rows():
 # ---------------------------------------------------------------------------
 # full-size workloads, as bench.py runs them
 # ---------------------------------------------------------------------------
-FULL = ["dsv4_flash_h64", "dsv4_flash_h128", "dsv4_pro"]
+FULL = ["dsv4_flash_h64", "dsv4_flash_h128", "dsv4_flash_h128_compact", "dsv4_pro"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -140,3 +140,29 @@ def test_full_size_sampled(name):
     if not np.all(np.any(gpu["dkv"][named] != 0, axis=1)):
         errors.append("dkv: a named row received nothing")
     assert not errors, f"{name}: " + "; ".join(errors)
+
+
+def test_full_size_layout_invariance():
+    """The headline's index sets in the compact layout (packed, with
+    topk_length) give the same results as the non-compact layout, up to the
+    summation order that the slot positions change."""
+    a = wl.make_problem("dsv4_flash_h128")
+    b = wl.make_problem("dsv4_flash_h128_compact")
+    say("[gpu] layout invariance: headline non-compact vs compact")
+    ga = run_gpu(a, DEV, nan_prefill=False)
+    gb = run_gpu(b, DEV, nan_prefill=False)
+    errors = []
+    for k in ("o", "dq", "dkv"):
+        x, y = ga[k].astype(np.float64), gb[k].astype(np.float64)
+        scale = np.abs(x).max()
+        if np.abs(x - y).max() > 1e-2 * scale:
+            errors.append(f"{k}: max diff {np.abs(x - y).max():.3g} vs max {scale:.3g}")
+        cos = float((x * y).sum() / (np.linalg.norm(x) * np.linalg.norm(y)))
+        if cos < 0.99999:
+            errors.append(f"{k}: cosine {cos:.7f}")
+    fin = np.isfinite(ga["lse"])
+    if not np.array_equal(fin, np.isfinite(gb["lse"])) or np.abs(ga["lse"][fin] - gb["lse"][fin]).max() > 1e-4:
+        errors.append("lse differs")
+    if np.abs(ga["d_sink"] - gb["d_sink"]).max() > 1e-3 * np.abs(ga["d_sink"]).max():
+        errors.append("d_sink differs")
+    assert not errors, "; ".join(errors)
