@@ -136,7 +136,7 @@ def main():
     value = total_flop / (ms_per_step * 1e-3) / 1e12
     work = stage_work(p, n_valid)
     dominant = max(stage_ms, key=lambda k: stage_ms[k])
-    roofline = roofline_for(dominant, stage_ms[dominant] * 1e-3, work[dominant])
+    roofline = roofline_for(dominant, stage_ms[dominant] * 1e-3, work[dominant], p.name)
     fwd_s = stage_ms["fwd"] * 1e-3
 
     cpu = None
@@ -216,17 +216,17 @@ def source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(stage):
+def measured_traffic(stage, workload):
     """HBM bytes per launch of the stage's kernel(s) from the committed counter
     profile (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
-    kernel sources changed since it was taken."""
+    kernel sources changed since it was taken or it covers another workload."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_dsv4_flash_h128.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except OSError:
         return None
-    if rec.get("source_sha256") != source_hash():
+    if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
         return None
     frags = STAGE_KERNEL[stage]
     vals = [k["bytes_per_launch"] for name, k in rec["kernels"].items()
@@ -234,7 +234,7 @@ def measured_traffic(stage):
     return int(sum(vals)) if vals else None
 
 
-def roofline_for(stage, seconds, work):
+def roofline_for(stage, seconds, work, workload):
     flop, nbytes = work
     t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
@@ -244,7 +244,7 @@ def roofline_for(stage, seconds, work):
         achieved, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     return {
         "kernel": stage, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
-        "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(stage),
+        "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(stage, workload),
         "avg_launch_us": round(seconds * 1e6, 1), "algorithmic_flop": flop,
         "algorithmic_bytes": int(nbytes),
     }

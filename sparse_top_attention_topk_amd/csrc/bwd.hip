@@ -102,19 +102,32 @@ __global__ __launch_bounds__(256) void rows_count_kernel(BwdArgs a) {
 }
 
 // Per row: running offsets over the chunks (chunk_cnt becomes the exclusive
-// prefix inside the row's segment) and the row total.
+// prefix inside the row's segment) and the row total.  A workgroup takes 32
+// rows; 8 threads per row scan 8 consecutive ranges of chunks and combine
+// their sums through LDS (accesses of the 32 rows of a chunk are coalesced).
 __global__ __launch_bounds__(256) void rows_chunkscan_kernel(BwdArgs a) {
-    const int r = (int)blockIdx.x * 256 + threadIdx.x;
-    if (r >= a.S_kv) return;
+    __shared__ int s_sum[8][32];
+    const int rl = threadIdx.x & 31, part = threadIdx.x >> 5;
+    const int r = (int)blockIdx.x * 32 + rl;
     const int nch = (a.T + a.tchunk - 1) / a.tchunk;
+    const int per = (nch + 7) / 8;
+    const int c0 = part * per < nch ? part * per : nch;
+    const int c1 = c0 + per < nch ? c0 + per : nch;
+    int sum = 0;
+    if (r < a.S_kv)
+        for (int c = c0; c < c1; ++c) sum += a.chunk_cnt[(size_t)c * a.S_kv + r];
+    s_sum[part][rl] = sum;
+    __syncthreads();
     int run = 0;
-    for (int c = 0; c < nch; ++c) {
+    for (int q = 0; q < part; ++q) run += s_sum[q][rl];
+    if (r >= a.S_kv) return;
+    for (int c = c0; c < c1; ++c) {
         int* p = a.chunk_cnt + (size_t)c * a.S_kv + r;
         const int v = *p;
         *p = run;
         run += v;
     }
-    a.row_cnt[r] = run;
+    if (part == 7) a.row_cnt[r] = run;
 }
 
 // Exclusive scans over the rows (one workgroup): row_off from the row totals,
@@ -874,7 +887,7 @@ hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t str
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(rows_count_kernel, dim3(nch), dim3(256), lds, stream, a);
-        hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 31) / 32), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
         hipLaunchKernelGGL(rows_parts_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
         hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);

@@ -275,6 +275,17 @@ PROBLEMS = {
                                               name="dsv4_flash_h128_T4096", **kw),
     "dsv4_pro": lambda **kw: make_dsv4(16384, 128, 512, 512, 1024, seed=3,
                                        name="dsv4_pro_h128_T16384", **kw),
+    # the grid of the pages' DeepSeek-V4 timing table (D_qk = D_v = 512 in every row):
+    # flash H=64 and H=128 (top-k 512), pro H=128 (top-k 1024), T = 4096 / 8192 / 16384
+    **{f"grid_flash_h64_T{T}": (lambda T: lambda **kw: make_dsv4(T, 64, 512, 512, 512, seed=40 + T // 4096,
+                                                                  name=f"grid_flash_h64_T{T}", **kw))(T)
+       for T in (4096, 8192, 16384)},
+    **{f"grid_flash_h128_T{T}": (lambda T: lambda **kw: make_dsv4(T, 128, 512, 512, 512, seed=50 + T // 4096,
+                                                                   name=f"grid_flash_h128_T{T}", **kw))(T)
+       for T in (4096, 8192, 16384)},
+    **{f"grid_pro_h128_T{T}": (lambda T: lambda **kw: make_dsv4(T, 128, 512, 512, 1024, seed=60 + T // 4096,
+                                                                 name=f"grid_pro_h128_T{T}", **kw))(T)
+       for T in (4096, 8192, 16384)},
     # the headline's index sets packed to the front with topk_length
     "dsv4_flash_h128_compact": lambda **kw: make_dsv4(4096, 128, 576, 512, 512, seed=2, compact=True,
                                                       name="dsv4_flash_h128_T4096_compact", **kw),
