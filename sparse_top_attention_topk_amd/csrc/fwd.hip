@@ -7,7 +7,11 @@
 //   2. gathers the rows of the NEXT block into the other of two LDS tiles with
 //      asynchronous direct global->LDS 16-byte loads, so that the gather of
 //      block b+1 is in flight while block b is computed (the pages find the
-//      gather latency to be the bottleneck, [flash-attn #2882] Performance);
+//      gather latency to be the bottleneck, [flash-attn #2882] Performance).
+//      The loads are issued one per k-step of the first half's S^T loop: the
+//      address unit takes a 1 KB row load in about 20 cycles, so issuing a
+//      wave's 18 loads back to back stalls it, while spread between MFMAs
+//      they cost almost nothing;
 //   3. computes S^T = K Q^T with bf16 MFMA (slots x heads, fp32 accumulate);
 //      each wave owns NT x 16 heads and keeps their Q in registers; padded
 //      heads (h >= H) are zero rows, so any H in 1..128 runs without padded
@@ -50,34 +54,43 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
                                           const bf16x8 (&qop)[NT][DQK / 32],
                                           f32x4 (&oacc)[512 / 16][NT], float (&m_ref)[NT],
                                           float (&rmax)[NT], float (&l_run)[NT],
-                                          float (&l_rnd)[NT], int lane) {
+                                          float (&l_rnd)[NT], int lane, __bf16* gtile,
+                                          const int* grows, __amdgpu_buffer_rsrc_t kvr, int wave) {
     using C = FwdCfg<DQK, NW, NT>;
     using Tile = typename C::Tile;
     const int g = lane >> 4;
+    static_assert(NW == 4, "the gather schedule assumes 16 main rows and 2 rope loads per wave");
+    const int gids = Tile::template row_ids<NW>(grows, wave, lane);
 
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        // S^T for slots 32 half .. +31; K operands one k-step ahead
+        // S^T for slots 32 half .. +31; K operands two k-steps ahead
         f32x4 sacc[2][NT];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = zero4();
-        bf16x8 kop[2][2];
+        constexpr int KD = 3;
+        bf16x8 kop[KD][2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) kop[0][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, 0);
+        for (int i = 0; i < KD - 1; ++i)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) kop[i][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, i);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < C::KS) {
+            const int cur = ks % KD;
+            if (ks + KD - 1 < C::KS) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    kop[cur ^ 1][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, ks + 1);
+                    kop[(ks + KD - 1) % KD][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, ks + KD - 1);
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[m][nt]);
+            // the next block's gather, spread over the first half's matrix work
+            if (half == 0 && ks < 16) Tile::template gather_main_row<NW>(gtile, gids, kvr, wave, lane, ks);
+            if (half == 0 && ks >= 16) Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, ks - 16);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -131,19 +144,23 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
             // the sum of the bf16 weights the MFMA actually uses: O is
             // normalised by it, so O stays an exact convex combination of the
             // gathered V rows (a near one-hot row reproduces its V row)
-            float rsum = 0.f;
+            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+            float rsum = l_rnd[nt];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) rsum += (float)pop[nt][j];
-            l_rnd[nt] += rsum;
+            for (int j = 0; j < 4; ++j)
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[nt][2 * j], pop[nt][2 * j + 1]}, one, rsum, false);
+            l_rnd[nt] = rsum;
         }
 
-        // O^T += V^T P^T over slots 32 half .. +31, V^T one column tile ahead
-        bf16x8 vop[2];
-        vop[0] = Tile::slot_op(tile, TL, 32 * half, 0);
+        // O^T += V^T P^T over slots 32 half .. +31, V^T three column tiles ahead
+        constexpr int VD = 4;
+        bf16x8 vop[VD];
+#pragma unroll
+        for (int i = 0; i < VD - 1; ++i) vop[i] = Tile::slot_op(tile, TL, 32 * half, i);
 #pragma unroll
         for (int mc = 0; mc < C::MC; ++mc) {
-            const int cur = mc & 1;
-            if (mc + 1 < C::MC) vop[cur ^ 1] = Tile::slot_op(tile, TL, 32 * half, mc + 1);
+            const int cur = mc % VD;
+            if (mc + VD - 1 < C::MC) vop[(mc + VD - 1) % VD] = Tile::slot_op(tile, TL, 32 * half, mc + VD - 1);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = mfma16(vop[cur], pop[nt], oacc[mc][nt]);
             __builtin_amdgcn_sched_barrier(0);
@@ -227,8 +244,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __syncthreads();
             int ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
-            if (b + 1 < nblk) Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
-            if (active) fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
+            // the next block's gather is issued from inside the math (after
+            // the last block it loads rows nobody reads, into a free tile)
+            if (active)
+                fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane,
+                                       s_tile1, s_rows[(b + 1) % 3], kvr, wave);
+            else
+                Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
             if (b + 2 < nblk && tid < BLK)
                 s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
             if (b + 1 >= nblk) break;
@@ -237,8 +259,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __syncthreads();
             ahead = tid < BLK ? raw_index(a, t, (b + 3) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
-            if (b + 2 < nblk) Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
-            if (active) fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane);
+            if (active)
+                fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd,
+                                       lane, s_tile0, s_rows[(b + 2) % 3], kvr, wave);
+            else
+                Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
             if (b + 3 < nblk && tid < BLK)
                 s_rows[(b + 3) % 3][tid] = valid_row(ahead, (b + 3) * BLK + tid, L, a.S_kv);
         }
@@ -251,6 +276,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             far |= rmax[nt] > m_ref[nt] + REF_SLACK;
         }
         if (pass == 0 && active && __builtin_amdgcn_ballot_w64(far) != 0 && lane == 0) s_rerun = 1;
+        wait_vmem();                    // the spare gather after the last block
         __syncthreads();                // tiles and s_rows are free; s_rerun is final
         if (pass == 1 || s_rerun == 0) break;
 #pragma unroll

@@ -143,24 +143,30 @@ struct KvTileSwz {
             r * (DQK * 2), 0, 0);
     }
 
-    // Issue this wave's rope loads (8 loads of 8 rows x 128 bytes, split over
-    // the waves).
+    // Rope load k (0 <= k < 8 / NW) of this wave: rows 8j .. 8j+7 of the
+    // rope region, j = k NW + wave, one 16-byte chunk per lane.
+    template <int NW>
+    __device__ static void gather_rope_one(__bf16* tile, const int* s_row, __amdgpu_buffer_rsrc_t rs,
+                                           int wave_s, int lane, int k) {
+        if constexpr (ROPE) {
+            static_assert(NW <= 8 && 8 % NW == 0, "rope loads must split evenly");
+            const int j = k * NW + wave_s;
+            const int row = 8 * j + (lane >> 3);
+            int r = s_row[row];
+            r = r < 0 ? 0 : r;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_void*)(reinterpret_cast<char*>(tile) + ROPE_OFF + 8 * j * ROPE_ROWB), 16,
+                r * (DQK * 2) + 1024 + (((lane & 7) ^ fr(row)) << 4), 0, 0, 0);
+        }
+    }
+
+    // All of this wave's rope loads (8 loads of 8 rows x 128 bytes, split
+    // over the waves).
     template <int NW>
     __device__ static void gather_rope(__bf16* tile, const int* s_row, __amdgpu_buffer_rsrc_t rs,
                                        int wave_s, int lane) {
-        if constexpr (ROPE) {
-            static_assert(NW <= 8 && 8 % NW == 0, "rope loads must split evenly");
 #pragma unroll
-            for (int k = 0; k < 8 / NW; ++k) {
-                const int j = k * NW + wave_s;                            // rows 8j .. 8j+7
-                const int row = 8 * j + (lane >> 3);
-                int r = s_row[row];
-                r = r < 0 ? 0 : r;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rs, (lds_void*)(reinterpret_cast<char*>(tile) + ROPE_OFF + 8 * j * ROPE_ROWB), 16,
-                    r * (DQK * 2) + 1024 + (((lane & 7) ^ fr(row)) << 4), 0, 0, 0);
-            }
-        }
+        for (int k = 0; k < 8 / NW; ++k) gather_rope_one<NW>(tile, s_row, rs, wave_s, lane, k);
     }
 
     // The whole gather of one tile by this wave (the NW waves together fill
