@@ -207,14 +207,40 @@ __device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
 }
 
 // The double-buffered gather loop of the kernels that gather KV tiles:
-// body(tile, rows, b, parity) runs block b from tile 0 (even b, parity 0) or
-// tile 1 (odd b, parity 1) while the next block's rows are in flight into the
-// other tile.  pre(b, parity) runs before the gather of block b is issued and
-// may issue global loads for block b (they complete before block b starts,
-// and waiting for them never waits for a gather issued after them).
+// body(tile, rows, b, parity, gtile, grows) runs block b from tile 0 (even b,
+// parity 0) or tile 1 (odd b, parity 1) and issues, spread over its math
+// (GatherSpread), this wave's share of the gather of block b + 1 from the
+// slot rows grows into the other tile gtile.  After the last block that
+// gather loads rows nobody reads into a tile that is free.  pre(b, parity)
+// runs before block b - 1's body and may issue global loads for block b
+// (they complete before block b starts, and waiting for them never waits for
+// a gather issued after them).
 struct NoPre {
     template <typename P>
     __device__ void operator()(int, P) const {}
+};
+
+// The next block's gather, one load per step of a matrix loop: main rows at
+// steps 0 .. RPW - 1, rope loads at the steps after (a 1 KB row load takes
+// the address unit about 20 cycles; issued back to back they stall the wave,
+// between MFMAs they cost almost nothing).
+template <int DQK, int NW>
+struct GatherSpread {
+    using Tile = KvTileSwz<DQK>;
+    static constexpr int RPW = Tile::template RPW<NW>;
+    static constexpr int STEPS = RPW + (Tile::ROPE ? 8 / NW : 0);
+    __bf16* gtile;
+    const int* grows;
+    __amdgpu_buffer_rsrc_t kvr;
+    int ids, wave, lane;
+    __device__ GatherSpread(__bf16* gt, const int* gr, __amdgpu_buffer_rsrc_t rs, int w, int l)
+        : gtile(gt), grows(gr), kvr(rs), ids(Tile::template row_ids<NW>(gr, w, l)), wave(w), lane(l) {}
+    // step is a compile-time constant after unrolling
+    __device__ void step(int s) const {
+        if (s < RPW) Tile::template gather_main_row<NW>(gtile, ids, kvr, wave, lane, s);
+        else if (s < STEPS) Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, s - RPW);
+    }
+    __device__ void all() const { Tile::template gather_async<NW>(gtile, grows, kvr, wave, lane); }
 };
 
 template <int DQK, int NW, typename Body, typename Pre = NoPre>
@@ -240,11 +266,8 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         int ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < nblk) {
-            pre(b + 1, P1{});
-            Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
-        }
-        body(s_tile0, s_rows[b % 3], b, P0{});
+        if (b + 1 < nblk) pre(b + 1, P1{});
+        body(s_tile0, s_rows[b % 3], b, P0{}, GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane));
         if (b + 2 < nblk && tid < BLK)
             s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
         if (b + 1 >= nblk) break;
@@ -252,14 +275,12 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) {
-            pre(b + 2, P0{});
-            Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
-        }
-        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{});
+        if (b + 2 < nblk) pre(b + 2, P0{});
+        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{}, GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane));
         if (b + 3 < nblk && tid < BLK)
             s_rows[(b + 3) % 3][tid] = valid_row_b(ahead, (b + 3) * BLK + tid, L, a.S_kv);
     }
+    wait_vmem();                 // the spare gather after the last block
 }
 
 // ---------------------------------------------------------------------------
@@ -273,9 +294,10 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
                                           const bf16x8 (&qop)[NT][DQK / 32],
                                           const bf16x8 (&dop)[NT][16], const float (&lse2)[NT],
                                           const float (&dlt)[NT], int t, int h_wave, int b,
-                                          int lane) {
+                                          int lane, const GatherSpread<DQK, NW>& gs) {
     using Tile = KvTileSwz<DQK>;
     constexpr int KS = DQK / 32, KV_ = 16;
+    static_assert(GatherSpread<DQK, NW>::STEPS <= KS, "the gather must fit in the first half's S loop");
     const int g = lane >> 4, n = lane & 15;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -303,6 +325,7 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
                     sacc[m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[m][nt]);
                     if (ks < KV_) dpacc[m][nt] = mfma16(kop[cur][m], dop[nt][ks], dpacc[m][nt]);
                 }
+            if (half == 0) gs.step(ks);
             __builtin_amdgcn_sched_barrier(0);
         }
         // P = 2^(s * scale * log2 e - LSE_tot * log2 e), masked; dS' = scale P (dP - Delta)
@@ -373,10 +396,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
     }
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto) {
+                             [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs) {
                                  if (active)
                                      sdp_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, dlt, t,
-                                                            h_wave, b, lane);
+                                                            h_wave, b, lane, gs);
+                                 else
+                                     gs.all();
                              });
 }
 
@@ -455,10 +480,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     };
 
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto par) {
+                             [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs) {
         (void)rows;
         (void)b;
-        if (!active) return;
+        if (!active) {
+            gs.all();
+            return;
+        }
+        static_assert(std::decay_t<decltype(gs)>::STEPS <= MCW, "the gather must fit in the column loop");
         bf16x8 kop[2][2];
         kload(tile, 0, kop[0]);
 #pragma unroll
@@ -470,6 +499,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
                 acc[mc][nt] = mfma16(kop[cur][0], dsop[par][0][nt], acc[mc][nt]);
                 acc[mc][nt] = mfma16(kop[cur][1], dsop[par][1][nt], acc[mc][nt]);
             }
+            gs.step(mc);
             __builtin_amdgcn_sched_barrier(0);
         }
     }, load_ds);
