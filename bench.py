@@ -193,7 +193,7 @@ STAGE_KERNEL = {"fwd": ("fwd_kernel",), "preprocess": ("preprocess_kernel",),
 def stage_work(p, n):
     """Algorithmic work per launch of each stage: (FLOP, bytes).  n = valid
     (token, slot) pairs.  Gathered KV rows count 2 * d_qk bytes per valid slot
-    (the pages' model); partials are 3 bytes per value per valid slot."""
+    (the pages' model); partials are 2 bytes per value per valid slot."""
     T, H, dqk, dv, S, W = p.T, p.H, p.d_qk, p.d_v, p.S_kv, p.W
     return {
         "fwd": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2),
@@ -201,8 +201,8 @@ def stage_work(p, n):
         "index_inversion": (0.0, 2 * T * W * 4 + n * 4),
         "sdp": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2 + 2 * H * n * 2),
         "dq": (2.0 * H * dqk * n, n * dqk * 2 + H * n * 2 + T * H * dqk * 2),
-        "dkv": (2.0 * H * (dqk + dv) * n, 2 * H * n * 2 + T * H * (dqk + dv) * 2 + n * dqk * 3),
-        "dkv_reduce": (0.0, n * dqk * 3 + n * 4 + S * dqk * 4),
+        "dkv": (2.0 * H * (dqk + dv) * n, 2 * H * n * 2 + T * H * (dqk + dv) * 2 + n * dqk * 2),
+        "dkv_reduce": (0.0, n * dqk * 2 + n * 4 + S * dqk * 4),
         "dsink": (0.0, 2 * T * H * 4),
     }
 

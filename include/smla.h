@@ -107,8 +107,9 @@ size_t smla_bwd_workspace_size(const smla_dims* dims);
  *   dkv        fp32 [S_kv, d_qk] out: row r is the sum, over the valid slots
  *              that name r taken in token order, of scale * dS^T q (all d_qk
  *              columns) plus P^T dO (first d_v columns); each slot's
- *              contribution is accumulated in fp32 and kept with 16 bits of
- *              significand (relative rounding <= 2^-16) until the row sum.
+ *              contribution is accumulated in fp32 and kept until the row
+ *              sum in blocks of 4 columns sharing an exponent, with error at
+ *              most 2^-13 of the block's largest magnitude.
  *              The order is fixed, so dkv is the same bits run to run.  Rows
  *              never named by a valid slot (e.g. row 0 for -1 sentinels) are
  *              exactly 0.

@@ -34,7 +34,7 @@ int token_chunk(int T) { return T > 256 ? (T + 255) / 256 : 1; }
 //   chunk_cnt        int32 [ceil(T / tchunk), S_kv], tchunk = ceil(T / 256)
 //   row_cnt          int32 [S_kv]; row_off int32 [S_kv + 1]
 //   entries          int32 [T * W]
-//   partial          [T * Wp] rows of d_qk 24-bit values (3 * d_qk bytes)
+//   partial          [T * Wp] rows of d_qk values in 4-value blocks (2 * d_qk bytes)
 //   part_off         int32 [S_kv + 1]; part_row int32 [max_parts]
 //   part_sum         fp32 [max_parts, d_qk], max_parts = T * W / 64 + S_kv
 struct WsLayout {
@@ -55,7 +55,7 @@ WsLayout ws_layout(const smla_dims* d) {
     L.off = align256(L.cnt + (size_t)d->S_kv * sizeof(int32_t));
     L.ent = align256(L.off + ((size_t)d->S_kv + 1) * sizeof(int32_t));
     L.part = align256(L.ent + (size_t)d->T * d->W * sizeof(int32_t));
-    L.poff = align256(L.part + (size_t)d->T * Wp * d->d_qk * 3);
+    L.poff = align256(L.part + (size_t)d->T * Wp * d->d_qk * 2);
     const size_t mp = (size_t)d->T * d->W / 64 + d->S_kv;
     L.max_parts = (int)mp;
     L.prow = align256(L.poff + ((size_t)d->S_kv + 1) * sizeof(int32_t));

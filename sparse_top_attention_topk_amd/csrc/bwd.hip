@@ -22,11 +22,13 @@
 //                accumulates dQ^T = K^T (scale dS)^T in registers
 //   bwd_dkv      one workgroup per token: contracts over all heads,
 //                u = (scale dS)^T q + P^T dO per valid slot (fp32 accumulate),
-//                written to the slot's row of a [T * Wp] partial buffer as
-//                24-bit values (fp32 rounded to nearest even at bit 8, so
-//                relative error <= 2^-16 per value; the row sums that follow
-//                add fp32 rounding of the same order, and the partial traffic,
-//                which bounds this half of the backward, drops by a quarter)
+//                written to the slot's row of a [T * Wp] partial buffer in
+//                16 bits per value (blocks of four values sharing the largest
+//                exponent, 14-bit signed multiples of 2^-12 of it: error at
+//                most 2^-13 of the block's largest magnitude, an order below
+//                the bf16 rounding of P and dS that the MFMAs already see; the
+//                partial traffic, which bounds this half of the backward, is
+//                half that of fp32)
 //   dkv_part / dkv_combine
 //                sum each row's listed partials in token order, in bounded
 //                parts (one wave each) and then per row; write dkv (rows no
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // per token through LDS with asynchronous loads (two buffers in flight).  The
 // P / dS tiles of the next block load asynchronously while the current block
 // is computed.  Each lane ends up holding 4 consecutive columns of u for one
-// slot and writes them as one 12-byte store (four 24-bit values) into the
+// slot and writes them as one 8-byte store (a 4-value block) into the
 // slot's row of the partial buffer; slots that are not valid are skipped.
 // ---------------------------------------------------------------------------
 
@@ -644,17 +646,17 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
             }
         }
         // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot 16 qt + n,
-        // stored as 24-bit values (12 bytes); only valid slots are written
+        // stored as one 4-value block (8 bytes); only valid slots are written
         // (the row lists name no other slot)
         const int slot = 16 * qt + n;
         const int v = raw[slot];
         if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
             char* dst = reinterpret_cast<char*>(a.partial) +
-                        ((size_t)t * a.Wp + b * BLK + slot) * (3 * DQK) + 3 * (c_wave + 4 * g);
+                        ((size_t)t * a.Wp + b * BLK + slot) * (2 * DQK) + 2 * (c_wave + 4 * g);
 #pragma unroll
             for (int nt = 0; nt < NTC; ++nt)
                 if (NTC * 8 == DQK / 16 || nt < ntc)            // the wave's own tiles
-                    *reinterpret_cast<u32x3*>(dst + 48 * nt) = pack24x4(acc[nt]);
+                    *reinterpret_cast<u32x2*>(dst + 32 * nt) = pack_blk4(acc[nt]);
         }
     }
 }
@@ -763,8 +765,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 template <int DQK>
 __global__ __launch_bounds__(256) void dkv_part_kernel(BwdArgs a) {
-    // lane l < DQK / 16 owns columns 16 l .. 16 l + 15: 48 packed bytes, three
-    // 16-byte loads per row
+    // lane l < DQK / 16 owns columns 16 l .. 16 l + 15: four 8-byte blocks,
+    // two 16-byte loads per row
     constexpr int G = DQK / 16;
     constexpr int U = 4;                       // partial rows in flight per wave
     const int p = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -780,21 +782,21 @@ __global__ __launch_bounds__(256) void dkv_part_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = zero4();
     for (int k0 = 0; k0 < cnt; k0 += U) {
-        u32x4 x[U][3];
+        u32x4 x[U][2];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int e = __shfl(my_ent, k0 + u, 64);
             const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.partial) +
-                                                              (size_t)e * (3 * DQK) + 48 * lane);
+                                                              (size_t)e * (2 * DQK) + 32 * lane);
 #pragma unroll
-            for (int v = 0; v < 3; ++v) x[u][v] = (k0 + u < cnt && act) ? src[v] : u32x4{0u, 0u, 0u, 0u};
+            for (int v = 0; v < 2; ++v) x[u][v] = (k0 + u < cnt && act) ? src[v] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            acc[0] += unpack24x4(u32x3{x[u][0][0], x[u][0][1], x[u][0][2]});
-            acc[1] += unpack24x4(u32x3{x[u][0][3], x[u][1][0], x[u][1][1]});
-            acc[2] += unpack24x4(u32x3{x[u][1][2], x[u][1][3], x[u][2][0]});
-            acc[3] += unpack24x4(u32x3{x[u][2][1], x[u][2][2], x[u][2][3]});
+            acc[0] += unpack_blk4(u32x2{x[u][0][0], x[u][0][1]});
+            acc[1] += unpack_blk4(u32x2{x[u][0][2], x[u][0][3]});
+            acc[2] += unpack_blk4(u32x2{x[u][1][0], x[u][1][1]});
+            acc[3] += unpack_blk4(u32x2{x[u][1][2], x[u][1][3]});
         }
     }
     if (act) {

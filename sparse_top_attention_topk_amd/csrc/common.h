@@ -108,27 +108,46 @@ __device__ __forceinline__ void stage_slot_idx(int* dst, const int32_t* idx, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (b * 64 + lane) * 4, 0, 0, 0);
 }
 
-// 24-bit storage of fp32 values (the dKV partials): the top 24 bits of the
-// fp32 pattern, rounded to nearest even on the 8 dropped bits, so a stored
-// value keeps sign, exponent and 15 mantissa bits (relative error <= 2^-16).
-// Four values pack into three dwords.
-__device__ __forceinline__ uint32_t f32_to_24(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+// Block storage of fp32 values in 16 bits each (the dKV partials): a group of
+// four values keeps the largest fp32 exponent field E among them (8 bits) and
+// each value as a 14-bit signed multiple of 2^(E - 139), i.e. of 2^-12 times
+// the group's leading power of two.  A value's error is at most 2^-13 of the
+// group's largest magnitude (2^-12 where rounding reaches the end of the
+// range).  Groups below 2^-114 are stored as zero; a group holding a
+// non-finite value decodes as NaN.  Layout: w0 = E | q0 << 8 | (q1 & 0x3FF)
+// << 22, w1 = q1 >> 10 | q2 << 4 | q3 << 18 (q in 14-bit two's complement).
+__device__ __forceinline__ u32x2 pack_blk4(f32x4 v) {
+    uint32_t e = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // (through a scalar: a bit cast of a vector element can read the
+        // wrong element with this compiler)
+        const float x = v[i];
+        const uint32_t ei = (__builtin_bit_cast(uint32_t, x) >> 23) & 0xFFu;
+        e = ei > e ? ei : e;
+    }
+    const float sc = __builtin_bit_cast(float, (266u - (e > 12u ? e : 13u)) << 23);   // 2^(139 - E)
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int qi = (int)__builtin_rintf(v[i] * sc);
+        qi = qi < -8191 ? -8191 : (qi > 8191 ? 8191 : qi);
+        q[i] = (uint32_t)qi & 0x3FFFu;
+    }
+    const u32x2 w = {e | (q[0] << 8) | (q[1] << 22), (q[1] >> 10) | (q[2] << 4) | (q[3] << 18)};
+    if (e == 255u) return u32x2{255u, 0u};
+    return e > 12u ? w : u32x2{0u, 0u};
 }
 
-__device__ __forceinline__ u32x3 pack24x4(f32x4 v) {
-    const uint32_t r0 = f32_to_24(v[0]), r1 = f32_to_24(v[1]), r2 = f32_to_24(v[2]), r3 = f32_to_24(v[3]);
-    return u32x3{r0 | (r1 << 24), (r1 >> 8) | (r2 << 16), (r2 >> 16) | (r3 << 8)};
-}
-
-__device__ __forceinline__ f32x4 unpack24x4(u32x3 w) {
-    const uint32_t r0 = w[0] & 0xFFFFFFu;
-    const uint32_t r1 = (w[0] >> 24) | ((w[1] & 0xFFFFu) << 8);
-    const uint32_t r2 = (w[1] >> 16) | ((w[2] & 0xFFu) << 16);
-    const uint32_t r3 = w[2] >> 8;
-    return f32x4{__builtin_bit_cast(float, r0 << 8), __builtin_bit_cast(float, r1 << 8),
-                 __builtin_bit_cast(float, r2 << 8), __builtin_bit_cast(float, r3 << 8)};
+__device__ __forceinline__ f32x4 unpack_blk4(u32x2 w) {
+    const uint32_t e = w[0] & 0xFFu;
+    float sc = e > 12u ? __builtin_bit_cast(float, (e - 12u) << 23) : 0.f;       // 2^(E - 139)
+    sc = e == 255u ? __builtin_nanf("") : sc;
+    const int q0 = __builtin_amdgcn_sbfe((int)w[0], 8, 14);
+    const int q1 = __builtin_amdgcn_sbfe((int)((w[0] >> 22) | (w[1] << 10)), 0, 14);
+    const int q2 = __builtin_amdgcn_sbfe((int)w[1], 4, 14);
+    const int q3 = __builtin_amdgcn_sbfe((int)w[1], 18, 14);
+    return f32x4{(float)q0 * sc, (float)q1 * sc, (float)q2 * sc, (float)q3 * sc};
 }
 
 // Finite-max-guarded logaddexp: ln(e^a + e^b); an infinite maximum is returned

@@ -36,7 +36,7 @@ struct BwdArgs {
     int* row_cnt;     // [S_kv]: valid slots naming each KV row
     int* row_off;     // [S_kv + 1]: segment starts of the row-grouped list
     int* entries;     // [T * W]: flat slot indices t * Wp + j, grouped by row
-    uint32_t* partial; // [T * Wp] rows of 3 * d_qk bytes: per-slot dKV contributions, 24-bit
+    uint32_t* partial; // [T * Wp] rows of 2 * d_qk bytes: per-slot dKV contributions, 4-value blocks
     int* part_off;    // [S_kv + 1]: first reduce part of each row
     int* part_row;    // [max_parts]: row of each reduce part
     float* part_sum;  // [max_parts, d_qk] fp32: sums of the parts

@@ -91,7 +91,7 @@ def _ws_expected(T, S_kv, H, d_qk, W):
     off = a(off + S_kv * 4)              # row counts
     off = a(off + (S_kv + 1) * 4)        # row offsets
     off = a(off + T * W * 4)             # row lists
-    off = a(off + T * Wp * d_qk * 3)     # partials (24-bit)
+    off = a(off + T * Wp * d_qk * 2)     # partials (16 bits per value)
     mp = T * W // 64 + S_kv
     off = a(off + (S_kv + 1) * 4)        # part offsets
     off = a(off + mp * 4)                # part rows
