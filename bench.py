@@ -127,6 +127,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the high-accuracy Delta (smla_bwd_delta_exact, in place of the
+    # preprocess): timed on its own after the steps, not part of `value`
+    delta_x = torch.empty_like(delta)
+    _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x, stream=stream)
+    ex0, ex1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ex0.record(stream)
+    for _ in range(3):
+        _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x, stream=stream)
+    ex1.record(stream)
+    torch.cuda.synchronize()
+    delta_exact_ms = ex0.elapsed_time(ex1) / 3
+
     names = ["fwd", "preprocess"] + list(_lib.BWD_STAGES)
     stage_ms = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, nm in enumerate(names)}
@@ -175,6 +187,8 @@ def main():
             "fwd_mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
             "fwd_flop": fwd_flop, "bwd_flop": bwd_flop, "gathered_bytes_fwd": gathered,
+            "delta_exact_us": round(delta_exact_ms * 1e3, 1),
+            "step_us_exact_delta_mode": round((step_ms - stage_ms["preprocess"] + delta_exact_ms) * 1e3, 1),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -187,7 +201,7 @@ STAGE_KERNEL = {"fwd": ("fwd_kernel",), "preprocess": ("preprocess_kernel",),
                 "index_inversion": ("rows_",), "sdp": ("bwd_sdp_kernel",),
                 "dq": ("bwd_dq_kernel",), "dkv": ("bwd_dkv_kernel",),
                 "dkv_reduce": ("dkv_part_kernel", "dkv_combine_kernel"),
-                "dsink": ("dsink_kernel",)}
+                "dsink": ("dsink_kernel",), "delta_exact": ("delta_exact_kernel",)}
 
 
 def stage_work(p, n):

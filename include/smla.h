@@ -95,6 +95,24 @@ smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
 smla_status smla_bwd_preprocess(const smla_dims* dims, const void* o, const void* dO,
                                 float* delta, void* stream);
 
+/* Exact Delta, the high-accuracy alternative to smla_bwd_preprocess
+ * [cuDNN-FE #785 Not addressed: the table of delta sources, second row].
+ * Recomputes, per token, the probabilities P_j (from lse and the sink as in
+ * smla_bwd) and dP_j = dO . V_j over the valid slots and returns
+ *   delta      fp32 [T, H] out: sum_j P_j dP_j, accumulated in fp32 (P_j in
+ *              fp32, not rounded to bf16); 0 for a token with no valid slot
+ * This equals O . dO for the exact O (the FlashAttention identity), without
+ * the bf16 rounding of the stored O that limits smla_bwd_preprocess; fed to
+ * smla_bwd it makes d_sink and the Delta term of dS exact to fp32 rounding.
+ * It costs one more pass of the S and dP products over the gathered rows.
+ * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16
+ * [T, H, d_v]; lse fp32 [T, H] from smla_fwd.  No workspace.
+ */
+smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const void* kv,
+                                 const void* dO, const float* lse, const int32_t* topk_idxs,
+                                 const int32_t* topk_length, const float* attn_sink,
+                                 float* delta, void* stream);
+
 /* Bytes of device workspace smla_bwd needs for these sizes (0 if T == 0).
  * Returns 0 for unsupported sizes as well; smla_bwd reports the error. */
 size_t smla_bwd_workspace_size(const smla_dims* dims);
@@ -117,7 +135,7 @@ size_t smla_bwd_workspace_size(const smla_dims* dims);
  *              p_sink = sigmoid(sink - lse); required iff attn_sink != NULL
  * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16
  * [T, H, d_v]; lse fp32 [T, H] from smla_fwd; delta fp32 [T, H] from
- * smla_bwd_preprocess.  workspace: device memory of at least
+ * smla_bwd_preprocess or smla_bwd_delta_exact.  workspace: device memory of at least
  * smla_bwd_workspace_size(dims) bytes, used by this call only.
  */
 smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const void* dO,

@@ -7,7 +7,8 @@ Python binding) imports, calls or links anything here.  Only the test suite,
 Modules
 -------
 ``smla``   per-token, per-slot definition of the forward and backward
-           (``oracle_fwd``, ``oracle_bwd``), written out in fp64 NumPy.
+           (``oracle_fwd``, ``oracle_bwd``) and of the exact Delta
+           (``oracle_delta_exact``), written out in fp64 NumPy.
 ``dense``  a second, independent formulation: dense masked attention over all
            KV rows in torch fp64, with autograd gradients.  It pins ``smla``.
 ``fd``     central finite differences of L = sum(dO * O), a third pin that
@@ -25,5 +26,6 @@ from .smla import (  # noqa: F401
     round_to_bf16,
     oracle_fwd,
     oracle_bwd,
+    oracle_delta_exact,
     fwd_flops,
 )

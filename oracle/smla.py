@@ -43,6 +43,7 @@ __all__ = [
     "round_to_bf16",
     "oracle_fwd",
     "oracle_bwd",
+    "oracle_delta_exact",
     "fwd_flops",
 ]
 
@@ -274,6 +275,35 @@ def oracle_bwd(q, kv, dO, topk_idxs, topk_length, attn_sink, scale, d_v,
         if sink is not None:
             d_sink -= p_sink(lse_cols, sink) * dl
     return dq, dkv, (d_sink if sink is not None else None), delta
+
+
+def oracle_delta_exact(q, kv, dO, topk_idxs, topk_length, attn_sink, scale, d_v, tokens=None):
+    """Delta[t,h] = sum_j p_j dP_j over the token's valid slots.
+
+    The second delta source of the table in [cuDNN-FE #785] Not addressed:
+    the probabilities p_j (with the sink in the denominator) times
+    dP_j = <dO[t,h,:], kv[idx_j,:d_v]>, summed over the valid slots, instead
+    of the product of dO with the stored output.  By the FlashAttention
+    identity it equals dO . O for the exact O.  An empty row gives 0.
+    Returns delta [T',H] (``tokens`` as in oracle_fwd).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    T, H, d_qk = q.shape
+    S_kv = kv.shape[0]
+    sink = None if attn_sink is None else np.asarray(attn_sink, dtype=np.float64)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    delta = np.zeros((len(toks), H))
+    for i, t in enumerate(toks):
+        ln = None if topk_length is None else topk_length[t]
+        _, rows = valid_slots(topk_idxs[t], ln, S_kv)
+        if rows.size == 0:
+            continue
+        _, _, _, p = _token_probs(q[t], kv, rows, scale, sink, d_qk)
+        dP = dO[t] @ kv[rows, :d_v].T                    # [H, K_t]
+        delta[i] = (p * dP).sum(axis=1)
+    return delta
 
 
 def fwd_flops(H: int, d_qk: int, d_v: int, n_valid_slots: int) -> float:

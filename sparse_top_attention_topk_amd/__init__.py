@@ -4,7 +4,8 @@ The compute path is the HIP library ``libsmla.so`` (C ABI in include/smla.h);
 ``_lib`` is its thin ctypes binding.  ``workloads`` draws seeded synthetic
 inputs.  Importing the binding requires the built library.
 """
-__all__ = ["smla_fwd", "smla_bwd_preprocess", "smla_bwd_workspace_size", "smla_bwd"]
+__all__ = ["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
+           "smla_bwd"]
 
 
 def __getattr__(name):

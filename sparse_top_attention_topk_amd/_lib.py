@@ -39,6 +39,8 @@ def _load():
     lib.smla_fwd.restype = ctypes.c_int
     lib.smla_bwd_preprocess.argtypes = [D, P, P, F32P, P]
     lib.smla_bwd_preprocess.restype = ctypes.c_int
+    lib.smla_bwd_delta_exact.argtypes = [D, P, P, P, F32P, I32P, I32P, F32P, F32P, P]
+    lib.smla_bwd_delta_exact.restype = ctypes.c_int
     lib.smla_bwd_workspace_size.argtypes = [D]
     lib.smla_bwd_workspace_size.restype = ctypes.c_size_t
     lib.smla_bwd.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
@@ -55,8 +57,8 @@ def _load():
 
 LIB = _load()
 
-EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_workspace_size", "smla_bwd",
-            "smla_bwd_profiled", "smla_status_string")
+EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
+            "smla_bwd", "smla_bwd_profiled", "smla_status_string")
 
 BWD_STAGES = ("index_inversion", "sdp", "dq", "dkv", "dkv_reduce", "dsink")
 
@@ -141,6 +143,35 @@ def smla_bwd_preprocess(o, dO, delta=None, stream=None, scale=1.0):
     dims = make_dims(T, 1, H, 576, d_v, 1, scale)
     _check(LIB.smla_bwd_preprocess(ctypes.byref(dims), _ptr(o), _ptr(dO), _ptr(delta),
                                    _stream(dev, stream)), "smla_bwd_preprocess")
+    return delta
+
+
+def smla_bwd_delta_exact(q, kv, dO, lse, topk_idxs, topk_length, attn_sink, scale, delta=None,
+                         stream=None):
+    """Exact Delta = sum_j P_j dP_j in fp32 (no bf16 O); returns delta [T,H]."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(kv, "kv", torch.bfloat16, dev, 2)
+    _need(dO, "dO", torch.bfloat16, dev, 3)
+    _need(lse, "lse", torch.float32, dev, 2)
+    _need(topk_idxs, "topk_idxs", torch.int32, dev, 2)
+    _need(topk_length, "topk_length", torch.int32, dev, 1)
+    _need(attn_sink, "attn_sink", torch.float32, dev, 1)
+    T, H, _ = q.shape
+    d_v = dO.shape[2]
+    if dO.shape[:2] != (T, H) or lse.shape != (T, H):
+        raise ValueError("dO and lse must match q's [T, H]")
+    if topk_idxs.shape[0] != T or (topk_length is not None and topk_length.shape[0] != T):
+        raise ValueError("topk_idxs / topk_length must have T rows")
+    if attn_sink is not None and attn_sink.shape[0] != H:
+        raise ValueError("attn_sink must have H entries")
+    if delta is None:
+        delta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(delta, "delta", torch.float32, dev, 2)
+    dims = _dims_from(q, kv, topk_idxs, scale, d_v)
+    _check(LIB.smla_bwd_delta_exact(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dO), _ptr(lse),
+                                    _ptr(topk_idxs), _ptr(topk_length), _ptr(attn_sink), _ptr(delta),
+                                    _stream(dev, stream)), "smla_bwd_delta_exact")
     return delta
 
 

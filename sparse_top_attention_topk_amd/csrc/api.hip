@@ -116,6 +116,32 @@ smla_status smla_bwd_preprocess(const smla_dims* d, const void* o, const void* d
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
+smla_status smla_bwd_delta_exact(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                                 const float* lse, const int32_t* topk_idxs,
+                                 const int32_t* topk_length, const float* attn_sink, float* delta,
+                                 void* stream) {
+    smla_status st = check_dims(d);
+    if (st != SMLA_OK) return st;
+    if (d->T == 0) return SMLA_OK;
+    if (!q || !kv || !dO || !lse || !topk_idxs || !delta) return SMLA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(kv) || !aligned16(dO)) return SMLA_ERR_ALIGN;
+    smla::BwdArgs a = {};
+    a.q = static_cast<const __bf16*>(q);
+    a.kv = static_cast<const __bf16*>(kv);
+    a.dO = static_cast<const __bf16*>(dO);
+    a.lse = lse;
+    a.delta_out = delta;
+    a.idx = topk_idxs;
+    a.len = topk_length;
+    a.sink = attn_sink;
+    a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
+    a.Wp = (int)round_up_blk(d->W);
+    a.scale = d->scale;
+    a.scale_log2 = d->scale * smla::LOG2E;
+    hipError_t e = smla::launch_delta_exact(d->d_qk, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
 size_t smla_bwd_workspace_size(const smla_dims* d) {
     if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
     return ws_layout(d).total;
@@ -138,7 +164,7 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
         if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SMLA_ERR_ALIGN;
     }
-    smla::BwdArgs a;
+    smla::BwdArgs a = {};
     a.q = static_cast<const __bf16*>(q);
     a.kv = static_cast<const __bf16*>(kv);
     a.dO = static_cast<const __bf16*>(dO);

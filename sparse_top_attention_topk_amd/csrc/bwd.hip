@@ -290,13 +290,13 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
 // q and dO stay in registers as the B operands of S^T = K Q^T and
 // dP^T = V dO^T.  Per 64-slot block, two halves of 32 slots.
 // ---------------------------------------------------------------------------
-template <int DQK, int NW, int NT>
+template <int DQK, int NW, int NT, bool EXACT>
 __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
                                           const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
                                           const bf16x8 (&qop)[NT][DQK / 32],
                                           const bf16x8 (&dop)[NT][16], const float (&lse2)[NT],
-                                          const float (&dlt)[NT], int t, int h_wave, int b,
-                                          int lane, const GatherSpread<DQK, NW>& gs) {
+                                          const float (&dlt)[NT], float (&pdp)[NT], int t, int h_wave,
+                                          int b, int lane, const GatherSpread<DQK, NW>& gs) {
     using Tile = KvTileSwz<DQK>;
     constexpr int KS = DQK / 32, KV_ = 16;
     static_assert(GatherSpread<DQK, NW>::STEPS <= KS, "the gather must fit in the first half's S loop");
@@ -330,6 +330,20 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
             if (half == 0) gs.step(ks);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (EXACT) {
+            // Delta = sum_j P_j dP_j over the token's valid slots, fp32
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
+                        const float p = ok ? fast_exp2(sacc[m][nt][i] * a.scale_log2 - lse2[nt]) : 0.f;
+                        pdp[nt] = __builtin_fmaf(p, dpacc[m][nt][i], pdp[nt]);
+                    }
+            continue;
+        }
         // P = 2^(s * scale * log2 e - LSE_tot * log2 e), masked; dS' = scale P (dP - Delta)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -357,8 +371,10 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
     }
 }
 
-template <int DQK, int NW, int NT>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
+// One token of bwd_sdp (EXACT = false) or of the exact-Delta pass (EXACT =
+// true: the same S and dP, summed as P dP per head instead of stored).
+template <int DQK, int NW, int NT, bool EXACT>
+__device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     using Tile = KvTileSwz<DQK>;
     constexpr int KS = DQK / 32, HT = NW * NT * 16;
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
@@ -374,7 +390,15 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
     const bool active = h_wave < a.H;
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
-    if (nblk == 0) return;                       // uniform: nothing to store
+    if (nblk == 0) {                             // uniform: nothing to store
+        if (EXACT && g == 0)                     // (Delta of an empty row: 0)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int head = h_wave + nt * 16 + n;
+                if (head < a.H) a.delta_out[(size_t)t * a.H + head] = 0.f;
+            }
+        return;
+    }
 
     bf16x8 qop[NT][KS], dop[NT][16];
     float lse2[NT], dlt[NT];
@@ -393,18 +417,42 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
             const float l = a.lse[row];
             const float lt = a.sink ? glae(l, a.sink[head]) : l;
             lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
-            dlt[nt] = a.delta[row];
+            if (!EXACT) dlt[nt] = a.delta[row];
         }
     }
+    float pdp[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
                              [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs) {
                                  if (active)
-                                     sdp_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, dlt, t,
-                                                            h_wave, b, lane, gs);
+                                     sdp_block<DQK, NW, NT, EXACT>(a, tile, TL, rows, qop, dop, lse2, dlt,
+                                                                   pdp, t, h_wave, b, lane, gs);
                                  else
                                      gs.all();
                              });
+    if constexpr (EXACT) {
+        // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float v = pdp[nt];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            const int head = h_wave + nt * 16 + n;
+            if (active && g == 0 && head < a.H) a.delta_out[(size_t)t * a.H + head] = v;
+        }
+    }
+}
+
+template <int DQK, int NW, int NT>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
+    sdp_token<DQK, NW, NT, false>(a);
+}
+
+template <int DQK, int NW, int NT>
+__global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
+    sdp_token<DQK, NW, NT, true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -896,6 +944,22 @@ static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev, h
     hipLaunchKernelGGL((dkv_part_kernel<DQK>), dim3((a.max_parts + 3) / 4), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((dkv_combine_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
     mark(5);
+}
+
+// Exact Delta: the S / dP half of bwd_sdp, accumulating sum_j P_j dP_j
+// instead of storing P and dS.
+template <int DQK>
+static void launch_delta_exact_t(const BwdArgs& a, hipStream_t stream) {
+    if (a.H > 64)
+        hipLaunchKernelGGL((delta_exact_kernel<DQK, 8, 1>), dim3(a.T, 1), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL((delta_exact_kernel<DQK, 4, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_delta_exact(int d_qk, const BwdArgs& a, hipStream_t stream) {
+    if (d_qk == 576) launch_delta_exact_t<576>(a, stream);
+    else launch_delta_exact_t<512>(a, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream,

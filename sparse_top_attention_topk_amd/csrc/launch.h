@@ -24,6 +24,7 @@ struct BwdArgs {
     const __bf16* dO;
     const float* lse;
     const float* delta;
+    float* delta_out; // [T, H]: exact Delta (written by launch_delta_exact only)
     const int32_t* idx;
     const int32_t* len;
     const float* sink;
@@ -49,6 +50,8 @@ struct BwdArgs {
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,
                              hipStream_t stream);
+// Delta[t, h] = sum_j P_j dP_j (uses q, kv, dO, lse, idx, len, sink, delta_out)
+hipError_t launch_delta_exact(int d_qk, const BwdArgs& a, hipStream_t stream);
 // ev: NULL, or SMLA_BWD_STAGES + 1 events recorded at the stage boundaries
 hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream,
                       hipEvent_t* ev);

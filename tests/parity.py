@@ -8,6 +8,10 @@ Bars (applied per output tensor):
   d_sink       max|gpu - ref| <= 1e-2 * max|ref| over the head vector
                (<= 1e-6 absolute when the reference is all zero)
   dKV rows     the set of rows with any nonzero value is identical
+With the exact Delta (smla_bwd_delta_exact), against the fp64 reference:
+  Delta        max|gpu - ref| <= 1e-4 * max|ref| (fp32 sums of fp32 terms),
+               and below the error of the bf16-O Delta
+  d_sink       max|gpu - ref| <= 1e-4 * max|ref|
 """
 from __future__ import annotations
 
@@ -61,6 +65,36 @@ def run_gpu(p, dev, nan_prefill=True):
                dkv=dkv.cpu().numpy(), delta=delta.cpu().numpy(),
                d_sink=None if d_sink is None else d_sink.cpu().numpy())
     return out
+
+
+def run_gpu_exact(p, dev):
+    """Forward, then the exact Delta (sum_j P_j dP_j) and the backward fed with
+    it; the preprocess Delta (bf16 O . dO) is returned too for comparison."""
+    from sparse_top_attention_topk_amd import _lib
+    d = to_dev(p, dev)
+    T, H = p.T, p.H
+    o, lse = _lib.smla_fwd(d["q"], d["kv"], d["idx"], d["length"], d["sink"], p.scale)
+    delta_pre = _lib.smla_bwd_preprocess(o, d["dO"])
+    delta = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    _lib.smla_bwd_delta_exact(d["q"], d["kv"], d["dO"], lse, d["idx"], d["length"], d["sink"],
+                              p.scale, delta=delta)
+    d_sink = None if d["sink"] is None else torch.empty((H,), dtype=torch.float32, device=dev)
+    dq, dkv, d_sink = _lib.smla_bwd(d["q"], d["kv"], d["dO"], lse, delta, d["idx"], d["length"],
+                                    d["sink"], p.scale, d_sink=d_sink)
+    torch.cuda.synchronize()
+    return dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.float().cpu().numpy(),
+                dkv=dkv.cpu().numpy(), delta=delta.cpu().numpy(), delta_pre=delta_pre.cpu().numpy(),
+                d_sink=None if d_sink is None else d_sink.cpu().numpy())
+
+
+def oracle_delta_exact(p, tokens=None):
+    """The oracle's exact Delta on all tokens or on a token subset (only those
+    tokens' rows are widened to fp64)."""
+    tk = torch.arange(p.T) if tokens is None else torch.from_numpy(np.asarray(tokens, dtype=np.int64))
+    return oracle.oracle_delta_exact(
+        p.q[tk].double().numpy(), p.kv.double().numpy(), p.dO[tk].double().numpy(),
+        p.topk_idxs[tk].numpy(), None if p.topk_length is None else p.topk_length[tk].numpy(),
+        None if p.attn_sink is None else p.attn_sink.double().numpy(), p.scale, p.d_v)
 
 
 def run_oracle(p, tokens=None, delta_from="bf16"):

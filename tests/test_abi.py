@@ -26,9 +26,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd",
-                                           "smla_bwd_workspace_size", "smla_bwd_profiled",
+    assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact",
+                                           "smla_bwd", "smla_bwd_workspace_size", "smla_bwd_profiled",
                                            "smla_status_string"])
+    from sparse_top_attention_topk_amd import _lib
+    assert sorted(_lib.EXPORTED) == declared_functions()
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -71,12 +73,20 @@ def test_null_pointers_and_alignment(lib):
     q = ctypes.c_void_p(0x1008)       # not 16-byte aligned
     assert lib.LIB.smla_fwd(ctypes.byref(d), q, p, p, None, None, p, p, None) == 4
     assert lib.LIB.smla_bwd_preprocess(ctypes.byref(d), None, p, p, None) == 1
+    # exact Delta: every input but topk_length / attn_sink is required, q kv dO aligned
+    assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(d), p, p, p, p, p, None, None, None, None) == 1
+    assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(d), p, p, None, p, p, None, None, p, None) == 1
+    assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(d), p, p, q, p, p, None, None, p, None) == 4
+    bad = _dims(lib, d_qk=128)
+    assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(bad), p, p, p, p, p, None, None, p, None) == 3
 
 
 def test_empty_problem_is_a_no_op(lib):
     d = _dims(lib, T=0)
     assert lib.LIB.smla_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
     assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == 0
+    assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(d), None, None, None, None, None, None, None,
+                                        None, None) == 0
 
 
 def _ws_expected(T, S_kv, H, d_qk, W):

@@ -10,8 +10,9 @@ import numpy as np
 import pytest
 import torch
 
-from parity import (compare_full, compare_exact_delta, run_gpu, run_oracle, say, check_tensor,
-                    check_lse, referenced_rows, tokens_referencing)
+from parity import (compare_full, compare_exact_delta, run_gpu, run_gpu_exact, run_oracle,
+                    oracle_delta_exact, say, check_tensor, check_lse, referenced_rows,
+                    tokens_referencing)
 from sparse_top_attention_topk_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +103,70 @@ def test_repeated_empty_and_mixed_rows():
             g = run_gpu(pp, DEV)
             assert np.array_equal(g["o"], rr["o"]) and np.array_equal(g["dq"], rr["dq"])
             np.testing.assert_allclose(g["dkv"], rr["dkv"], rtol=0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# exact Delta (smla_bwd_delta_exact) and the backward fed with it
+# ---------------------------------------------------------------------------
+EXACT_TOL = 1e-4
+EXACT_CASES = {
+    "tiny-sink": lambda: wl.make_tiny(seed=0, sink=True),
+    "tiny-compact": lambda: wl.make_tiny(seed=0, sink=True, compact=True),
+    "edge-compact-h24": lambda: wl.make_edge_compact(24),
+    "edge-compact-h128": lambda: wl.make_edge_compact(128),
+    "edge-wide-h64": lambda: wl.make_edge_wide(64),
+    "edge-sink-h24": lambda: wl.make_edge_sink(24),
+    "width-118-h128": lambda: wl.make_edge_width118(128),
+}
+
+
+@pytest.mark.parametrize("name", list(EXACT_CASES))
+def test_exact_delta(name):
+    p = EXACT_CASES[name]()
+    say(f"[gpu] exact delta {name}: T={p.T} H={p.H} W={p.W} compact={p.topk_length is not None}")
+    g = run_gpu_exact(p, DEV)
+    ref = run_oracle(p, delta_from="fp64")
+    d_ref = oracle_delta_exact(p)
+    errors = compare_full(g, ref)
+    m = np.abs(d_ref).max()
+    e = np.abs(g["delta"] - d_ref).max()
+    e_pre = np.abs(g["delta_pre"] - d_ref).max()
+    say(f"[gpu] exact delta {name}: max err {e:.3e}, bf16-O delta {e_pre:.3e}, max|delta| {m:.3e}")
+    if not np.all(np.isfinite(g["delta"])):
+        errors.append("delta: non-finite entries")
+    elif e > EXACT_TOL * m + 1e-7:
+        errors.append(f"delta: max err {e:.3e} vs max {m:.3e}")
+    if e_pre > 0 and e >= e_pre:
+        errors.append(f"delta: exact {e:.3e} not below bf16-O {e_pre:.3e}")
+    if g["d_sink"] is not None:
+        ms = np.abs(ref["d_sink"]).max()
+        es = np.abs(g["d_sink"] - ref["d_sink"]).max()
+        say(f"[gpu] exact delta {name}: d_sink max err {es:.3e} vs max {ms:.3e}")
+        if es > EXACT_TOL * ms + 1e-7:
+            errors.append(f"d_sink: max err {es:.3e} vs max {ms:.3e}")
+    if p.topk_length is not None:
+        empty = np.nonzero(p.topk_length.numpy() <= 0)[0]
+        if empty.size and not np.all(g["delta"][empty] == 0):
+            errors.append("delta: empty rows are not 0")
+    assert not errors, f"{name}: " + "; ".join(errors)
+
+
+def test_exact_delta_full_size_sampled():
+    """The headline workload: exact Delta on sampled tokens against the oracle."""
+    from sparse_top_attention_topk_amd import _lib
+    p = wl.make_problem("dsv4_flash_h128")
+    say(f"[gpu] exact delta full-size: T={p.T} H={p.H}")
+    q, kv, dO, idx = p.q.to(DEV), p.kv.to(DEV), p.dO.to(DEV), p.topk_idxs.to(DEV)
+    sink = p.attn_sink.to(DEV)
+    _, lse = _lib.smla_fwd(q, kv, idx, None, sink, p.scale)
+    delta = _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, None, sink, p.scale).cpu().numpy()
+    toks = np.unique(np.concatenate([[0, 1, 127, 128, p.T // 2, p.T - 1],
+                                     np.random.default_rng(8).integers(0, p.T, 6)]))
+    d_ref = oracle_delta_exact(p, tokens=toks)
+    m = np.abs(d_ref).max()
+    e = np.abs(delta[toks] - d_ref).max()
+    say(f"[gpu] exact delta full-size: max err {e:.3e} vs max {m:.3e}")
+    assert np.all(np.isfinite(delta)) and e <= EXACT_TOL * m
 
 
 # ---------------------------------------------------------------------------

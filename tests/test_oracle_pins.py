@@ -464,6 +464,81 @@ def test_token_subset_matches_full_run():
 
 
 # ---------------------------------------------------------------------------
+# exact Delta (sum_j p_j dP_j)
+# ---------------------------------------------------------------------------
+def run_delta_exact(p, **kw):
+    return oracle.oracle_delta_exact(p["q"], p["kv"], p["dO"], p["topk_idxs"], p["topk_length"],
+                                     p["attn_sink"], p["scale"], p["d_v"], **kw)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_delta_exact_equals_dense_output_dot_do(case):
+    """Delta = dO . O with O from the dense masked brute force (a formulation
+    that shares no code with the per-slot sum); empty rows give 0."""
+    p = small_problem(40 + case, **CASES[case])
+    d = run_delta_exact(p)
+    Od, lsed, _, _ = dense_of(p)
+    exp = (p["dO"] * Od).sum(axis=2)
+    exp[~np.isfinite(lsed)] = 0.0          # empty rows: no slot, no Delta
+    np.testing.assert_allclose(d, exp, rtol=0, atol=1e-12)
+
+
+def test_delta_exact_closed_forms():
+    # one valid slot, no sink: p = 1, Delta = dO . v
+    p = small_problem(44, sink=None, empty_rows=False)
+    T, W = p["topk_idxs"].shape
+    rng = np.random.default_rng(45)
+    idx = np.full((T, W), -1, dtype=np.int32)
+    rows = rng.integers(0, p["kv"].shape[0], T)
+    for t in range(T):
+        idx[t, rng.integers(0, W)] = rows[t]
+    p["topk_idxs"] = idx
+    d = run_delta_exact(p)
+    exp = (p["dO"] * p["kv"][rows, None, : p["d_v"]]).sum(axis=2)
+    np.testing.assert_allclose(d, exp, rtol=0, atol=1e-13)
+    # a saturating positive sink takes all the mass: Delta = 0
+    p = small_problem(46, sink=[float("inf"), 3.0e38, 2.4e38], empty_rows=False)
+    assert np.all(run_delta_exact(p) == 0)
+    # a token subset gives the same rows
+    p = small_problem(47)
+    sub = np.array([6, 2, 3])
+    np.testing.assert_array_equal(run_delta_exact(p, tokens=sub), run_delta_exact(p)[sub])
+
+
+def test_delta_exact_vs_bf16_output_delta():
+    """The bf16-rounded O of the default backward moves Delta by about 2^-9
+    relative; the exact form agrees with the fp64-O backward's Delta."""
+    p = small_problem(48)
+    d = run_delta_exact(p)
+    _, _, _, d64 = run_bwd(p, delta_from="fp64")
+    _, _, _, d16 = run_bwd(p, delta_from="bf16")
+    np.testing.assert_allclose(d, d64, rtol=0, atol=1e-12)
+    assert np.abs(d16 - d).max() > 1e-6 * np.abs(d).max()
+
+
+def test_planted_delta_mistakes_are_caught():
+    """Sum over every slot position (sentinels aliased to row 0), or softmax
+    without the sink: both must fail the dense pin."""
+    p = small_problem(49)
+    Od, lsed, _, _ = dense_of(p)
+    exp = (p["dO"] * Od).sum(axis=2)
+    exp[~np.isfinite(lsed)] = 0.0
+    T, H, d_qk = p["q"].shape
+    bad_alias = np.zeros((T, H))
+    bad_nosink = np.zeros((T, H))
+    for t in range(T):
+        rows_all = np.clip(p["topk_idxs"][t].astype(np.int64), 0, None)
+        _, _, _, pa = smla._token_probs(p["q"][t], p["kv"], rows_all, p["scale"], p["attn_sink"], d_qk)
+        bad_alias[t] = (pa * (p["dO"][t] @ p["kv"][rows_all, : p["d_v"]].T)).sum(1)
+        _, rows = smla.valid_slots(p["topk_idxs"][t], None, p["kv"].shape[0])
+        if rows.size:
+            _, _, _, pn = smla._token_probs(p["q"][t], p["kv"], rows, p["scale"], None, d_qk)
+            bad_nosink[t] = (pn * (p["dO"][t] @ p["kv"][rows, : p["d_v"]].T)).sum(1)
+    assert not np.allclose(bad_alias, exp, rtol=0, atol=1e-12)
+    assert not np.allclose(bad_nosink, exp, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # values the pages print
 # ---------------------------------------------------------------------------
 def test_pages_sink_threshold_and_limits():
