@@ -263,24 +263,30 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         pre(0, P0{});
         Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
     }
+    // Block k: wait for its tile; store the slot rows of block k + 1 (their
+    // raw indices were loaded at block k - 1, and the wait just covered that
+    // load: storing them any earlier would wait for the whole gather issued
+    // since); load the raw indices of block k + 2; run the body, which issues
+    // the gather of block k + 1.
+    int ahead = 0;
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
+        if (b > 0 && b + 1 < nblk && tid < BLK)
+            s_rows[(b + 1) % 3][tid] = valid_row_b(ahead, (b + 1) * BLK + tid, L, a.S_kv);
         __syncthreads();
-        int ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
+        ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 1 < nblk) pre(b + 1, P1{});
         body(s_tile0, s_rows[b % 3], b, P0{}, GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane));
-        if (b + 2 < nblk && tid < BLK)
-            s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
         if (b + 1 >= nblk) break;
         wait_vmem();
+        if (b + 2 < nblk && tid < BLK)
+            s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 2 < nblk) pre(b + 2, P0{});
         body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{}, GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane));
-        if (b + 3 < nblk && tid < BLK)
-            s_rows[(b + 3) % 3][tid] = valid_row_b(ahead, (b + 3) * BLK + tid, L, a.S_kv);
     }
     wait_vmem();                 // the spare gather after the last block
 }
@@ -581,6 +587,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
 // is computed.  Each lane ends up holding 4 consecutive columns of u for one
 // slot and writes them as one 8-byte store (a 4-value block) into the
 // slot's row of the partial buffer; slots that are not valid are skipped.
+// The stores go through a buffer resource over the token's partial rows
+// (a 32-bit lane offset, the block and quarter in the scalar offset): a
+// 64-bit row pointer per lane would not fit the register budget, and a
+// spilled one reloads with a wait on every outstanding load and store.
 // ---------------------------------------------------------------------------
 
 // P or scale*dS tile: [HP heads][64 slots] bf16, 128-byte rows, chunk c of row
@@ -638,21 +648,25 @@ __device__ __forceinline__ bf16x8 stage_op(const __bf16* stage, int c0, int lane
 }
 
 // Issue the loads of the [P | scale dS] tiles of block b into buf (rows
-// h < H of each; pieces of 8 head rows = 1 KB).  No wait here.
+// h < H of each; pieces of 8 head rows = 1 KB, a fixed number per wave so
+// the loop unrolls and keeps no loop state in registers).  No wait here.
 template <int HP, int NW>
 __device__ __forceinline__ void pd_tiles_async(const BwdArgs& a, __bf16* buf, int t, int b,
                                                int wave_s, int lane) {
-    const int np = (a.H + 7) >> 3;                 // pieces per tile
+    constexpr int NP = HP / 8;                     // pieces per tile (8 head rows each)
+    static_assert((2 * NP) % NW == 0, "pieces must split evenly over the waves");
     const int row_in = lane >> 3, pc = lane & 7;
-    for (int i = wave_s; i < 2 * np; i += NW) {
-        const int which = i >= np;                 // 0: P, 1: scale dS
-        const int k = i - which * np;
-        const int h = 8 * k + row_in;
+#pragma unroll
+    for (int k = 0; k < 2 * NP / NW; ++k) {
+        const int i = k * NW + wave_s;
+        const int which = i >= NP;                 // 0: P, 1: scale dS
+        const int piece = i - which * NP;
+        const int h = 8 * piece + row_in;
         if (h < a.H) {
             const __bf16* src = (which ? a.ws_ds : a.ws_p) + ((size_t)t * a.H + h) * a.Wp + b * BLK +
                                 ((pc ^ pf(h)) << 3);
             __builtin_amdgcn_global_load_lds((const void*)src,
-                                             (lds_void*)(buf + which * HP * BLK + 8 * k * BLK), 16, 0, 0);
+                                             (lds_void*)(buf + which * HP * BLK + 8 * piece * BLK), 16, 0, 0);
         }
     }
 }
@@ -671,8 +685,8 @@ __device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int 
 template <int DQK, int HK, int NTC>
 __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, const int* raw,
                                           const bf16x8 (&qB)[HK][NTC],
-                                          const bf16x8 (&dB)[HK][NTC], int t, int b, int L,
-                                          int c_wave, int ntc, int lane) {
+                                          const bf16x8 (&dB)[HK][NTC], int b, int L,
+                                          __amdgpu_buffer_rsrc_t prs, int voff, int ntc, int lane) {
     constexpr int HP = 32 * HK;
     const int g = lane >> 4, n = lane & 15;
     // four quarters of 16 slots: one accumulator tile per column tile
@@ -699,12 +713,11 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
         const int slot = 16 * qt + n;
         const int v = raw[slot];
         if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
-            char* dst = reinterpret_cast<char*>(a.partial) +
-                        ((size_t)t * a.Wp + b * BLK + slot) * (2 * DQK) + 2 * (c_wave + 4 * g);
+            const int soff = (b * BLK + 16 * qt) * (2 * DQK);
 #pragma unroll
             for (int nt = 0; nt < NTC; ++nt)
                 if (NTC * 8 == DQK / 16 || nt < ntc)            // the wave's own tiles
-                    *reinterpret_cast<u32x2*>(dst + 32 * nt) = pack_blk4(acc[nt]);
+                    __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[nt]), prs, voff + 32 * nt, soff, 0);
         }
     }
 }
@@ -781,7 +794,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         }
     }
 
-    // ---- blocks: [P | dS] tiles double-buffered
+    // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
+    // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
+    // slot 16 qt + n, columns c_wave + 16 nt + 4g .. +3
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<char*>(a.partial) + (size_t)t * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
+        0x00020000);
+    const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 4 * (lane >> 4));
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         __syncthreads();
@@ -789,7 +808,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
         }
-        dkv_block<DQK, HK, NTC>(a, s_pd0, s_raw[0], qB, dB, t, b, L, c_wave, ntc, lane);
+        dkv_block<DQK, HK, NTC>(a, s_pd0, s_raw[0], qB, dB, b, L, prs, voff, ntc, lane);
         if (b + 1 >= nblk) break;
         wait_vmem();
         __syncthreads();
@@ -797,7 +816,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
         }
-        dkv_block<DQK, HK, NTC>(a, s_pd1, s_raw[1], qB, dB, t, b + 1, L, c_wave, ntc, lane);
+        dkv_block<DQK, HK, NTC>(a, s_pd1, s_raw[1], qB, dB, b + 1, L, prs, voff, ntc, lane);
     }
 }
 

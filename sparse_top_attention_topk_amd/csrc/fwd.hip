@@ -235,27 +235,31 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
 
         // Two blocks per iteration so that each tile is a distinct LDS object.
-        // Per block: wait for this block's tile, start the next block's
-        // gather, fetch the slot rows two blocks ahead (issued before the
-        // gather, stored after the math), compute.
+        // Block k: wait for its tile; store the slot rows of block k + 1
+        // (their raw indices were loaded at block k - 1 and the wait just
+        // covered that load: storing them any earlier would wait for the whole
+        // gather issued since); load the raw indices of block k + 2; compute,
+        // issuing the gather of block k + 1 from inside the math (after the
+        // last block it loads rows nobody reads, into a free tile).
+        int ahead = 0;
         for (int b = 0; b < nblk; b += 2) {
             // ---- block b in tile 0
             wait_vmem();
+            if (b > 0 && b + 1 < nblk && tid < BLK)
+                s_rows[(b + 1) % 3][tid] = valid_row(ahead, (b + 1) * BLK + tid, L, a.S_kv);
             __syncthreads();
-            int ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
+            ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
-            // the next block's gather is issued from inside the math (after
-            // the last block it loads rows nobody reads, into a free tile)
             if (active)
                 fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane,
                                        s_tile1, s_rows[(b + 1) % 3], kvr, wave);
             else
                 Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
-            if (b + 2 < nblk && tid < BLK)
-                s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
             if (b + 1 >= nblk) break;
             // ---- block b+1 in tile 1
             wait_vmem();
+            if (b + 2 < nblk && tid < BLK)
+                s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
             __syncthreads();
             ahead = tid < BLK ? raw_index(a, t, (b + 3) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
@@ -264,8 +268,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
                                        lane, s_tile0, s_rows[(b + 2) % 3], kvr, wave);
             else
                 Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
-            if (b + 3 < nblk && tid < BLK)
-                s_rows[(b + 3) % 3][tid] = valid_row(ahead, (b + 3) * BLK + tid, L, a.S_kv);
         }
 
         // did any head's scores rise more than REF_SLACK above its reference?
