@@ -730,11 +730,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int NTC = (NTILES + NW - 1) / NW;         // tiles per wave, at most (5 or 4)
     constexpr int R = NTILES - NW * (NTC - 1);          // waves that take NTC tiles
     constexpr int HP = 32 * HK;                         // heads padded
-    __shared__ __attribute__((aligned(16))) __bf16 s_st0[32 * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 s_st1[32 * DQK];
-    __shared__ __attribute__((aligned(16))) __bf16 s_pd0[2 * HP * BLK];   // [P | dS], even blocks
-    __shared__ __attribute__((aligned(16))) __bf16 s_pd1[2 * HP * BLK];   // [P | dS], odd blocks
-    __shared__ int s_raw[2][BLK];                                          // raw top-k indices
+    // four LDS buffers of one size: s_st0, s_st1 and s_pd1 take the staged
+    // q / dO pieces in turn (three in flight); afterwards s_pd0 / s_pd1 hold
+    // the [P | dS] tiles of even / odd blocks
+    constexpr int SLOT = 32 * DQK > 2 * HP * BLK ? 32 * DQK : 2 * HP * BLK;
+    __shared__ __attribute__((aligned(16))) __bf16 s_st0[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 s_st1[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 s_pd0[SLOT];   // [P | dS], even blocks
+    __shared__ __attribute__((aligned(16))) __bf16 s_pd1[SLOT];   // [P | dS], odd blocks; staging
+    __shared__ int s_raw[2][BLK];                                  // raw top-k indices
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -750,49 +754,72 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int ntc = wave < R ? NTC : NTC - 1;
     const int c_wave = 16 * tile0;
 
-    // heads past H: their P / dS tile rows stay zero (never loaded)
-    if (HP > a.H) {
-        for (int i = tid; i < 2 * HP * BLK / 8; i += NW * 64) {
-            reinterpret_cast<u32x4*>(s_pd0)[i] = u32x4{0u, 0u, 0u, 0u};
-            reinterpret_cast<u32x4*>(s_pd1)[i] = u32x4{0u, 0u, 0u, 0u};
+    // heads past H: their P / dS tile rows stay zero (never loaded; s_pd1 is
+    // cleared after its turn as a staging buffer)
+    auto zero_rows_past_h = [&](__bf16* buf) {
+        for (int i = a.H * BLK / 8 + tid; i < HP * BLK / 8; i += NW * 64) {
+            reinterpret_cast<u32x4*>(buf)[i] = u32x4{0u, 0u, 0u, 0u};
+            reinterpret_cast<u32x4*>(buf + HP * BLK)[i] = u32x4{0u, 0u, 0u, 0u};
         }
-    }
+    };
+    if (HP > a.H) zero_rows_past_h(s_pd0);
 
     // ---- q and dO with heads in-lane: lane (g, n) of k-step hk, column tile
     // nt holds X[32hk + 8g + j][c_wave + 16nt + n], j = 0..7.  Staged in 2*HK
     // pieces of 32 head rows (rows past H repeat row H-1: their P and dS are
-    // zero), two buffers in flight.
+    // zero) through a ring of three buffers: piece p + 2 loads while piece p
+    // is read and piece p + 1 lands.  The [P | dS] tile of block 0 loads first
+    // (into s_pd0, outside the ring), so it is there when the pieces are.
     bf16x8 qB[HK][NTC], dB[HK][NTC];
-    auto issue = [&](int piece, __bf16* buf) {
+    constexpr int NPC = 2 * HK;
+    __bf16* const ring[3] = {s_st0, s_st1, s_pd1};
+    auto issue = [&](int piece) {
         const int hk = piece >> 1;
         const int nv = a.H - 32 * hk;
         const size_t row0 = (size_t)t * a.H + 32 * hk;
-        if ((piece & 1) == 0) stage_rows_async<DQK, NW>(buf, a.q + row0 * DQK, nv, wave, lane);
-        else stage_rows_async<DV, NW>(buf, a.dO + row0 * DV, nv, wave, lane);
+        if ((piece & 1) == 0) stage_rows_async<DQK, NW>(ring[piece % 3], a.q + row0 * DQK, nv, wave, lane);
+        else stage_rows_async<DV, NW>(ring[piece % 3], a.dO + row0 * DV, nv, wave, lane);
     };
+    // each wave issues at least 4 loads per piece (d_qk or d_v columns x 32
+    // rows in 16-byte loads over 8 waves): waiting down to 4 outstanding
+    // loads completes every load issued before the last piece (loads complete
+    // in issue order)
+    static_assert((32 * (DV / 8) / 64) / NW >= 4, "the ring waits assume at least 4 loads per piece");
     __syncthreads();                      // zero-fill done before any tile load lands
-    issue(0, s_st0);
+    pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
+    if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, 0, lane);
+    issue(0);
+    if (NPC > 1) issue(1);
 #pragma unroll
-    for (int piece = 0; piece < 2 * HK; ++piece) {
-        __bf16* cur = (piece & 1) ? s_st1 : s_st0;
-        __bf16* nxt = (piece & 1) ? s_st0 : s_st1;
-        wait_vmem();
-        __syncthreads();
-        if (piece + 1 < 2 * HK) {
-            issue(piece + 1, nxt);
+    for (int piece = 0; piece < NPC; ++piece) {
+        if (piece + 1 < NPC) {
+            // piece + 1 stays in flight.  A plain barrier: the workgroup fence
+            // of __syncthreads would wait for every outstanding LDS-bound
+            // load.  lgkmcnt(0): this wave's reads of piece - 1 are done
+            // before its buffer is reloaded.
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         } else {
-            pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
-            if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, 0, lane);
+            wait_vmem();
+            __syncthreads();
         }
+        if (piece + 2 < NPC) issue(piece + 2);            // into the buffer of piece - 1
+        const __bf16* cur = ring[piece % 3];
         const int hk = piece >> 1;
+        // operands are read unconditionally (column clamped into the piece)
+        // and zeroed after: no branch around the LDS reads
 #pragma unroll
         for (int nt = 0; nt < NTC; ++nt) {
             const int c0 = c_wave + 16 * nt;
-            const bool own = nt < ntc;
-            if ((piece & 1) == 0) qB[hk][nt] = own ? stage_op<DQK>(cur, c0, lane) : zero8();
-            else dB[hk][nt] = own && c0 < DV ? stage_op<DV>(cur, c0, lane) : zero8();
+            if ((piece & 1) == 0) {
+                const bf16x8 x = stage_op<DQK>(cur, c0 < DQK ? c0 : 0, lane);
+                qB[hk][nt] = nt < ntc ? x : zero8();
+            } else {
+                const bf16x8 x = stage_op<DV>(cur, c0 < DV ? c0 : 0, lane);
+                dB[hk][nt] = nt < ntc && c0 < DV ? x : zero8();
+            }
         }
     }
+    if (HP > a.H) zero_rows_past_h(s_pd1);   // the block loop's barrier orders it
 
     // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
     // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
