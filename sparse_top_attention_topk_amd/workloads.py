@@ -26,7 +26,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Problem", "make_problem", "PROBLEMS", "EDGE_HEADS"]
+__all__ = ["Problem", "make_problem", "make_batched", "segment", "PROBLEMS", "EDGE_HEADS"]
 
 EDGE_HEADS = (1, 24, 64, 96, 128)
 
@@ -259,6 +259,49 @@ def make_dsv4(T, H, d_qk, d_v, topk, seed, window=128, sink=True, compact=False,
                    meta=dict(seed=seed, window=window, topk=topk, compact=compact))
 
 
+def make_batched(H=64, lengths=(300, 77, 650), window=64, topk=128, d_qk=576, d_v=512, seed=70,
+                 compact=False):
+    """Several sequences packed into one problem (the varlen / batched case):
+    the tokens and KV rows of the sequences are concatenated and every index
+    is global.  Each sequence has S_kv = its length, causal [window | top-k]
+    rows of its own (the dsv4 recipe at a smaller window and top-k), shifted
+    by the sequence's first KV row; -1 stays -1.  ``meta["segments"]`` holds
+    the [start, end) token (and KV row) range of each sequence."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(lengths))
+    q, kv, dO, s = _dense(rng, T, T, H, d_qk, d_v, True)
+    W = window + topk
+    idx = np.full((T, W), -1, dtype=np.int32)
+    segs, t0 = [], 0
+    for n in lengths:
+        part = _window_topk_idxs(rng, n, window, topk)
+        idx[t0:t0 + n] = np.where(part >= 0, part + t0, -1)
+        segs.append((t0, t0 + n))
+        t0 += n
+    length = None
+    if compact:
+        valid = idx >= 0
+        ln = valid.sum(axis=1).astype(np.int32)
+        packed = np.full_like(idx, -1)
+        for t in range(T):
+            packed[t, : ln[t]] = idx[t][valid[t]]
+        idx, length = packed, torch.from_numpy(ln)
+    return Problem(f"batched_H{H}_{'_'.join(map(str, lengths))}", T, T, H, d_qk, d_v, W,
+                   1.0 / math.sqrt(d_qk), q, kv, dO, torch.from_numpy(idx), length, s,
+                   meta=dict(seed=seed, segments=segs, window=window, topk=topk, compact=compact))
+
+
+def segment(p: Problem, i: int) -> Problem:
+    """Sequence i of a batched problem as a problem of its own (local indices)."""
+    a, b = p.meta["segments"][i]
+    idx = p.topk_idxs[a:b].clone()
+    idx = torch.where(idx >= 0, idx - a, idx)
+    return Problem(f"{p.name}_seg{i}", b - a, b - a, p.H, p.d_qk, p.d_v, p.W, p.scale,
+                   p.q[a:b].clone(), p.kv[a:b].clone(), p.dO[a:b].clone(), idx,
+                   None if p.topk_length is None else p.topk_length[a:b].clone(),
+                   p.attn_sink, meta=dict(parent=p.name, segment=i))
+
+
 def make_problem(name: str, **kw) -> Problem:
     return PROBLEMS[name](**kw)
 
@@ -269,6 +312,7 @@ PROBLEMS = {
     "edge_compact": make_edge_compact,
     "edge_wide": make_edge_wide,
     "edge_sink": make_edge_sink,
+    "batched": make_batched,
     "dsv4_flash_h64": lambda **kw: make_dsv4(4096, 64, 512, 512, 512, seed=1,
                                              name="dsv4_flash_h64_T4096", **kw),
     "dsv4_flash_h128": lambda **kw: make_dsv4(4096, 128, 576, 512, 512, seed=2,

@@ -105,6 +105,22 @@ def test_repeated_empty_and_mixed_rows():
             np.testing.assert_allclose(g["dkv"], rr["dkv"], rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("compact", [False, True])
+def test_batched_sequences(compact):
+    """Three sequences packed with global indices: parity with the oracle, and
+    each sequence's O, LSE, dQ and dKV rows are the bits of that sequence run
+    alone (the same slots in the same order); d_sink is the sum over them."""
+    p = wl.make_batched(compact=compact)
+    gpu, ref = _run_and_compare(p, f"batched-compact{int(compact)}")
+    ds_sum = np.zeros_like(gpu["d_sink"])
+    for i, (a, b) in enumerate(p.meta["segments"]):
+        g = run_gpu(wl.segment(p, i), DEV)
+        for k in ("o", "lse", "dq", "dkv"):
+            assert np.array_equal(gpu[k][a:b], g[k]), f"segment {i}: {k} differs"
+        ds_sum += g["d_sink"]
+    np.testing.assert_allclose(gpu["d_sink"], ds_sum, rtol=1e-5, atol=1e-5)
+
+
 # ---------------------------------------------------------------------------
 # exact Delta (smla_bwd_delta_exact) and the backward fed with it
 # ---------------------------------------------------------------------------

@@ -539,6 +539,37 @@ def test_planted_delta_mistakes_are_caught():
 
 
 # ---------------------------------------------------------------------------
+# batches as concatenated sequences with global indices
+# ---------------------------------------------------------------------------
+def test_batched_problem_equals_its_sequences():
+    """Several sequences packed with global indices ([cuDNN-FE #298]: global
+    row indices over total_S_kv) give, per sequence, exactly the results of
+    that sequence alone; dKV rows of a sequence only receive its own tokens and
+    d_sink is the sum over the sequences."""
+    from sparse_top_attention_topk_amd import workloads as wl
+    for compact in (False, True):
+        p = wl.make_batched(H=2, lengths=(9, 4, 12), window=4, topk=6, seed=71, compact=compact)
+        x = p.np_inputs()
+        O, lse, _ = oracle.oracle_fwd(x["q"], x["kv"], x["topk_idxs"], x["topk_length"], x["attn_sink"],
+                                      x["scale"], x["d_v"])
+        dq, dkv, ds, _ = oracle.oracle_bwd(x["q"], x["kv"], x["dO"], x["topk_idxs"], x["topk_length"],
+                                           x["attn_sink"], x["scale"], x["d_v"])
+        ds_sum = np.zeros_like(ds)
+        for i, (a, b) in enumerate(p.meta["segments"]):
+            y = wl.segment(p, i).np_inputs()
+            Oi, lsei, _ = oracle.oracle_fwd(y["q"], y["kv"], y["topk_idxs"], y["topk_length"],
+                                            y["attn_sink"], y["scale"], y["d_v"])
+            dqi, dkvi, dsi, _ = oracle.oracle_bwd(y["q"], y["kv"], y["dO"], y["topk_idxs"],
+                                                  y["topk_length"], y["attn_sink"], y["scale"], y["d_v"])
+            np.testing.assert_allclose(O[a:b], Oi, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[a:b], lsei, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(dq[a:b], dqi, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(dkv[a:b], dkvi, rtol=0, atol=1e-13)
+            ds_sum += dsi
+        np.testing.assert_allclose(ds, ds_sum, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # values the pages print
 # ---------------------------------------------------------------------------
 def test_pages_sink_threshold_and_limits():
