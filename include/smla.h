@@ -144,6 +144,23 @@ smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const
                      float* dkv, float* d_sink, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* smla_bwd_preprocess followed by smla_bwd in one call [cuDNN-FE #785 Not
+ * addressed: Delta = O . dO; Summary 1-3 for the backward]: the kernel that
+ * recomputes P and dP also forms Delta = sum_c o . dO in fp32 from the rows
+ * it loads anyway, so the separate pass over O and dO is saved.
+ *   o          bf16 [T, H, d_v] in: the forward's output (from smla_fwd)
+ *   delta      fp32 [T, H] out: sum_c o[t,h,c] * dO[t,h,c] (what
+ *              smla_bwd_preprocess writes; the summation order differs, so
+ *              the bits may differ in the last places)
+ * Every other argument, output, the workspace and the errors are those of
+ * smla_bwd; o must be non-NULL and 16-byte aligned when T > 0.
+ */
+smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv,
+                            const void* dO, const void* o, const float* lse, float* delta,
+                            const int32_t* topk_idxs, const int32_t* topk_length,
+                            const float* attn_sink, void* dq, float* dkv, float* d_sink,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Number of stages smla_bwd runs, in order: index inversion, S/P/dP/dS,
  * dQ, per-slot dKV contributions, dKV row reduce, d_sink. */
 #define SMLA_BWD_STAGES 6

@@ -5,7 +5,7 @@ The compute path is the HIP library ``libsmla.so`` (C ABI in include/smla.h);
 inputs.  Importing the binding requires the built library.
 """
 __all__ = ["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
-           "smla_bwd"]
+           "smla_bwd", "smla_bwd_from_o"]
 
 
 def __getattr__(name):

@@ -46,6 +46,9 @@ def _load():
     lib.smla_bwd.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
                              ctypes.c_size_t, P]
     lib.smla_bwd.restype = ctypes.c_int
+    lib.smla_bwd_from_o.argtypes = [D, P, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
+                                    ctypes.c_size_t, P]
+    lib.smla_bwd_from_o.restype = ctypes.c_int
     lib.smla_bwd_profiled.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
                                       ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_void_p),
                                       ctypes.c_int]
@@ -58,7 +61,7 @@ def _load():
 LIB = _load()
 
 EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
-            "smla_bwd", "smla_bwd_profiled", "smla_status_string")
+            "smla_bwd", "smla_bwd_from_o", "smla_bwd_profiled", "smla_status_string")
 
 BWD_STAGES = ("index_inversion", "sdp", "dq", "dkv", "dkv_reduce", "dsink")
 
@@ -223,6 +226,46 @@ def smla_bwd(q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, scale, dq
             *[ctypes.c_void_p(e.cuda_event) for e in stage_events])
         _check(LIB.smla_bwd_profiled(*args, handles, len(stage_events)), "smla_bwd_profiled")
     return dq, dkv, d_sink
+
+
+def smla_bwd_from_o(q, kv, dO, o, lse, topk_idxs, topk_length, attn_sink, scale, delta=None, dq=None,
+                    dkv=None, d_sink=None, workspace=None, stream=None):
+    """smla_bwd_preprocess + smla_bwd in one call (Delta formed inside the
+    backward from ``o``); returns (dq, dkv, d_sink or None, delta fp32 [T,H])."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(kv, "kv", torch.bfloat16, dev, 2)
+    _need(dO, "dO", torch.bfloat16, dev, 3)
+    _need(o, "o", torch.bfloat16, dev, 3)
+    _need(lse, "lse", torch.float32, dev, 2)
+    _need(topk_idxs, "topk_idxs", torch.int32, dev, 2)
+    _need(topk_length, "topk_length", torch.int32, dev, 1)
+    _need(attn_sink, "attn_sink", torch.float32, dev, 1)
+    T, H, d_qk = q.shape
+    d_v = dO.shape[2]
+    dims = _dims_from(q, kv, topk_idxs, scale, d_v)
+    if delta is None:
+        delta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dkv is None:
+        dkv = torch.empty((kv.shape[0], d_qk), dtype=torch.float32, device=dev)
+    if attn_sink is not None and d_sink is None:
+        d_sink = torch.empty((H,), dtype=torch.float32, device=dev)
+    _need(delta, "delta", torch.float32, dev, 2)
+    _need(dq, "dq", torch.bfloat16, dev, 3)
+    _need(dkv, "dkv", torch.float32, dev, 2)
+    _need(d_sink, "d_sink", torch.float32, dev, 1)
+    need = int(LIB.smla_bwd_workspace_size(ctypes.byref(dims)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev, 1)
+    _check(LIB.smla_bwd_from_o(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse),
+                               _ptr(delta), _ptr(topk_idxs), _ptr(topk_length), _ptr(attn_sink),
+                               _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(workspace),
+                               ctypes.c_size_t(workspace.numel()), _stream(dev, stream)),
+           "smla_bwd_from_o")
+    return dq, dkv, d_sink, delta
 
 
 def smla_bwd_profiled(*args, stage_events, **kw):

@@ -147,8 +147,10 @@ size_t smla_bwd_workspace_size(const smla_dims* d) {
     return ws_layout(d).total;
 }
 
+// o == NULL: delta is an input (from the preprocess or the exact pass).
+// o != NULL: the S/dP kernel computes Delta = sum O dO and writes it to delta.
 static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, const void* dO,
-                            const float* lse, const float* delta, const int32_t* topk_idxs,
+                            const void* o, const float* lse, float* delta, const int32_t* topk_idxs,
                             const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
                             float* d_sink, void* workspace, size_t workspace_bytes, void* stream,
                             void* const* events) {
@@ -160,6 +162,7 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
         if (!q || !kv || !dO || !lse || !delta || !topk_idxs || !dq) return SMLA_ERR_NULL;
         if (!aligned16(q) || !aligned16(kv) || !aligned16(dO) || !aligned16(dq) || !aligned16(dkv))
             return SMLA_ERR_ALIGN;
+        if (o != nullptr && !aligned16(o)) return SMLA_ERR_ALIGN;
         const size_t need = smla_bwd_workspace_size(d);
         if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SMLA_ERR_ALIGN;
@@ -170,6 +173,8 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
     a.dO = static_cast<const __bf16*>(dO);
     a.lse = lse;
     a.delta = delta;
+    a.o = static_cast<const __bf16*>(o);
+    a.delta_out = o != nullptr ? delta : nullptr;
     a.idx = topk_idxs;
     a.len = topk_length;
     a.sink = attn_sink;
@@ -202,7 +207,16 @@ smla_status smla_bwd(const smla_dims* d, const void* q, const void* kv, const vo
                      const float* lse, const float* delta, const int32_t* topk_idxs,
                      const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
                      float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_impl(d, q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, dq, dkv, d_sink,
+    return bwd_impl(d, q, kv, dO, nullptr, lse, const_cast<float*>(delta), topk_idxs, topk_length, attn_sink,
+                    dq, dkv, d_sink, workspace, workspace_bytes, stream, nullptr);
+}
+
+smla_status smla_bwd_from_o(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                            const void* o, const float* lse, float* delta, const int32_t* topk_idxs,
+                            const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
+                            float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
+    if (d != nullptr && d->T > 0 && o == nullptr) return SMLA_ERR_NULL;
+    return bwd_impl(d, q, kv, dO, o, lse, delta, topk_idxs, topk_length, attn_sink, dq, dkv, d_sink,
                     workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -215,8 +229,8 @@ smla_status smla_bwd_profiled(const smla_dims* d, const void* q, const void* kv,
     if (n_events < SMLA_BWD_STAGES + 1) return SMLA_ERR_SHAPE;
     for (int i = 0; i <= SMLA_BWD_STAGES; ++i)
         if (stage_events[i] == nullptr) return SMLA_ERR_NULL;
-    return bwd_impl(d, q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, dq, dkv, d_sink,
-                    workspace, workspace_bytes, stream, stage_events);
+    return bwd_impl(d, q, kv, dO, nullptr, lse, const_cast<float*>(delta), topk_idxs, topk_length, attn_sink,
+                    dq, dkv, d_sink, workspace, workspace_bytes, stream, stage_events);
 }
 
 }  // extern "C"

@@ -245,10 +245,17 @@ struct GatherSpread {
     __device__ void all() const { Tile::template gather_async<NW>(gtile, grows, kvr, wave, lane); }
 };
 
-template <int DQK, int NW, typename Body, typename Pre = NoPre>
+// post() runs once, right after the first block's gather is issued: work that
+// waits for its own loads there overlaps them with that gather.
+struct NoPost {
+    __device__ void operator()() const {}
+};
+
+template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
                                                 int (*s_rows)[BLK], int t, int L, int nblk,
-                                                int wave, int lane, Body&& body, Pre&& pre = Pre{}) {
+                                                int wave, int lane, Body&& body, Pre&& pre = Pre{},
+                                                Post&& post = Post{}) {
     using Tile = KvTileSwz<DQK>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -262,6 +269,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     if (nblk > 0) {
         pre(0, P0{});
         Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+        post();
     }
     // Block k: wait for its tile; store the slot rows of block k + 1 (their
     // raw indices were loaded at block k - 1, and the wait just covered that
@@ -377,6 +385,35 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
     }
 }
 
+// Delta = sum over the d_v columns of O dO in fp32 (the preprocess pass's
+// arithmetic, fused into the S/dP kernel): lane (g, n) takes columns
+// 32 ks + 8g .. +7 of head h_wave + 16 nt + n (the layout of the dO operands,
+// which dO_at(nt, ks, row) returns), then the four lane groups are summed.
+// Writes delta_out for the existing heads and returns the sums in dlt.
+template <int NT, typename DOAt>
+__device__ __forceinline__ void fused_delta(const BwdArgs& a, int t, int h_wave, int lane, DOAt&& dO_at,
+                                            float (&dlt)[NT]) {
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int head = h_wave + nt * 16 + n;
+        const bool hv = head < a.H;
+        const size_t row = (size_t)t * a.H + (hv ? head : 0);
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const bf16x8 x = hv ? ld8(a.o + row * 512 + 32 * ks + 8 * g) : zero8();
+            const bf16x8 y = hv ? dO_at(nt, ks, row) : zero8();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];
+        }
+        acc += __shfl_xor(acc, 16, 64);
+        acc += __shfl_xor(acc, 32, 64);
+        dlt[nt] = acc;
+        if (hv && g == 0) a.delta_out[row] = acc;
+    }
+}
+
 // One token of bwd_sdp (EXACT = false) or of the exact-Delta pass (EXACT =
 // true: the same S and dP, summed as P dP per head instead of stored).
 template <int DQK, int NW, int NT, bool EXACT>
@@ -403,29 +440,50 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
                 const int head = h_wave + nt * 16 + n;
                 if (head < a.H) a.delta_out[(size_t)t * a.H + head] = 0.f;
             }
+        if (!EXACT && a.o != nullptr) {          // O dO still, as the preprocess pass would
+            float unused[NT];
+            fused_delta<NT>(a, t, h_wave, lane,
+                            [&](int, int ks, size_t row) { return ld8(a.dO + row * 512 + 32 * ks + 8 * g); },
+                            unused);
+        }
         return;
     }
 
+    // q, dO (and the LSE, Delta scalars) go to registers once the first
+    // tile's gather is in flight.  With o given, Delta = sum O dO is formed
+    // from dO before q is loaded (dO, O and q at once would not fit the
+    // registers): one more round trip than loading q and dO together, which
+    // costs about what the separate preprocess pass does.
     bf16x8 qop[NT][KS], dop[NT][16];
     float lse2[NT], dlt[NT];
+    auto post = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int head = h_wave + nt * 16 + n;
-        const bool hv = head < a.H;
-        const size_t row = (size_t)t * a.H + (hv ? head : 0);
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            const bool hv = head < a.H;
+            const size_t row = (size_t)t * a.H + (hv ? head : 0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = hv ? ld8(a.q + row * DQK + 32 * ks + 8 * g) : zero8();
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) dop[nt][ks] = hv ? ld8(a.dO + row * 512 + 32 * ks + 8 * g) : zero8();
-        lse2[nt] = 0.f;
-        dlt[nt] = 0.f;
-        if (hv) {
-            const float l = a.lse[row];
-            const float lt = a.sink ? glae(l, a.sink[head]) : l;
-            lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
-            if (!EXACT) dlt[nt] = a.delta[row];
+            for (int ks = 0; ks < 16; ++ks) dop[nt][ks] = hv ? ld8(a.dO + row * 512 + 32 * ks + 8 * g) : zero8();
+            lse2[nt] = 0.f;
+            dlt[nt] = 0.f;
+            if (hv) {
+                const float l = a.lse[row];
+                const float lt = a.sink ? glae(l, a.sink[head]) : l;
+                lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
+                if (!EXACT && a.o == nullptr) dlt[nt] = a.delta[row];
+            }
         }
-    }
+        if (!EXACT && a.o != nullptr)            // uniform
+            fused_delta<NT>(a, t, h_wave, lane, [&](int nt, int ks, size_t) { return dop[nt][ks]; }, dlt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            const bool hv = head < a.H;
+            const size_t row = (size_t)t * a.H + (hv ? head : 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = hv ? ld8(a.q + row * DQK + 32 * ks + 8 * g) : zero8();
+        }
+    };
     float pdp[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
@@ -437,7 +495,7 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
                                                                    pdp, t, h_wave, b, lane, gs);
                                  else
                                      gs.all();
-                             });
+                             }, NoPre{}, post);
     if constexpr (EXACT) {
         // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
 #pragma unroll

@@ -24,7 +24,9 @@ struct BwdArgs {
     const __bf16* dO;
     const float* lse;
     const float* delta;
-    float* delta_out; // [T, H]: exact Delta (written by launch_delta_exact only)
+    float* delta_out; // [T, H]: Delta written by the kernel that computes it (exact pass, or
+                      // the S/dP kernel when o is set)
+    const __bf16* o;  // [T, H, d_v] or NULL: the S/dP kernel computes Delta = sum O dO itself
     const int32_t* idx;
     const int32_t* len;
     const float* sink;

@@ -67,6 +67,27 @@ def run_gpu(p, dev, nan_prefill=True):
     return out
 
 
+def run_gpu_from_o(p, dev):
+    """Forward, then smla_bwd_from_o (Delta formed inside the backward); the
+    preprocess Delta is returned too (delta_pre) for comparison."""
+    from sparse_top_attention_topk_amd import _lib
+    d = to_dev(p, dev)
+    T, H = p.T, p.H
+    o, lse = _lib.smla_fwd(d["q"], d["kv"], d["idx"], d["length"], d["sink"], p.scale)
+    delta_pre = _lib.smla_bwd_preprocess(o, d["dO"])
+    delta = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    dq = torch.full((T, H, p.d_qk), float("nan"), dtype=torch.bfloat16, device=dev)
+    dkv = torch.full((p.S_kv, p.d_qk), float("nan"), dtype=torch.float32, device=dev)
+    d_sink = None if d["sink"] is None else torch.full((H,), float("nan"), dtype=torch.float32, device=dev)
+    dq, dkv, d_sink, delta = _lib.smla_bwd_from_o(d["q"], d["kv"], d["dO"], o, lse, d["idx"], d["length"],
+                                                  d["sink"], p.scale, delta=delta, dq=dq, dkv=dkv,
+                                                  d_sink=d_sink)
+    torch.cuda.synchronize()
+    return dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.float().cpu().numpy(),
+                dkv=dkv.cpu().numpy(), delta=delta.cpu().numpy(), delta_pre=delta_pre.cpu().numpy(),
+                d_sink=None if d_sink is None else d_sink.cpu().numpy())
+
+
 def run_gpu_exact(p, dev):
     """Forward, then the exact Delta (sum_j P_j dP_j) and the backward fed with
     it; the preprocess Delta (bf16 O . dO) is returned too for comparison."""

@@ -27,8 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact",
-                                           "smla_bwd", "smla_bwd_workspace_size", "smla_bwd_profiled",
-                                           "smla_status_string"])
+                                           "smla_bwd", "smla_bwd_from_o", "smla_bwd_workspace_size",
+                                           "smla_bwd_profiled", "smla_status_string"])
     from sparse_top_attention_topk_amd import _lib
     assert sorted(_lib.EXPORTED) == declared_functions()
 
@@ -79,6 +79,13 @@ def test_null_pointers_and_alignment(lib):
     assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(d), p, p, q, p, p, None, None, p, None) == 4
     bad = _dims(lib, d_qk=128)
     assert lib.LIB.smla_bwd_delta_exact(ctypes.byref(bad), p, p, p, p, p, None, None, p, None) == 3
+    # backward from O: o is required and 16-byte aligned; then the workspace check of smla_bwd
+    from_o = lib.LIB.smla_bwd_from_o
+    assert from_o(ctypes.byref(d), p, p, p, None, p, p, p, None, None, p, p, None, p, 0, None) == 1
+    assert from_o(ctypes.byref(d), p, p, p, q, p, p, p, None, None, p, p, None, p, 0, None) == 4
+    assert from_o(ctypes.byref(d), p, p, p, p, p, None, p, None, None, p, p, None, p, 0, None) == 1
+    assert from_o(ctypes.byref(d), p, p, p, p, p, p, p, None, None, p, p, None, p, 0, None) == 5
+    assert from_o(ctypes.byref(bad), p, p, p, p, p, p, p, None, None, p, p, None, p, 0, None) == 3
 
 
 def test_empty_problem_is_a_no_op(lib):

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from parity import (compare_full, compare_exact_delta, run_gpu, run_gpu_exact, run_oracle,
+from parity import (compare_full, compare_exact_delta, run_gpu, run_gpu_exact, run_gpu_from_o, run_oracle,
                     oracle_delta_exact, say, check_tensor, check_lse, referenced_rows,
                     tokens_referencing)
 from sparse_top_attention_topk_amd import workloads as wl
@@ -165,6 +165,65 @@ def test_exact_delta(name):
         if empty.size and not np.all(g["delta"][empty] == 0):
             errors.append("delta: empty rows are not 0")
     assert not errors, f"{name}: " + "; ".join(errors)
+
+
+FROM_O_CASES = {
+    "tiny-sink": lambda: wl.make_tiny(seed=0, sink=True, compact=False),
+    "tiny-compact": lambda: wl.make_tiny(seed=0, sink=True, compact=True),
+    "edge-compact-h24": lambda: wl.make_edge_compact(24),
+    "edge-wide-h128": lambda: wl.make_edge_wide(128),
+    "edge-sink-h64": lambda: wl.make_edge_sink(64),
+    "width-118-h128": lambda: wl.make_edge_width118(128),
+    "batched": lambda: wl.make_batched(),
+}
+
+
+@pytest.mark.parametrize("name", list(FROM_O_CASES))
+def test_bwd_from_o(name):
+    """smla_bwd_from_o against the oracle (the smla_bwd bars), and its Delta
+    against smla_bwd_preprocess's (same fp32 sums in another order)."""
+    p = FROM_O_CASES[name]()
+    say(f"[gpu] bwd from o {name}: T={p.T} H={p.H} W={p.W} compact={p.topk_length is not None}")
+    g = run_gpu_from_o(p, DEV)
+    errors = compare_full(g, run_oracle(p))
+    m = np.abs(g["delta_pre"]).max()
+    e = np.abs(g["delta"] - g["delta_pre"]).max()
+    say(f"[gpu] bwd from o {name}: delta vs preprocess max diff {e:.3e}, max|delta| {m:.3e}")
+    if not np.all(np.isfinite(g["delta"])):
+        errors.append("delta: non-finite entries")
+    elif e > 1e-5 * m + 1e-7:
+        errors.append(f"delta: max diff {e:.3e} vs preprocess, max {m:.3e}")
+    assert not errors, f"{name}: " + "; ".join(errors)
+
+
+def test_bwd_from_o_full_size():
+    """The headline workload (the launch configuration bench.py times):
+    smla_bwd_from_o against preprocess + smla_bwd on the same forward output,
+    which test_full_size_sampled holds to the oracle.  Delta to fp32 rounding;
+    dq, dkv, d_sink within the oracle bars (a Delta difference in the last
+    places can move a bf16 rounding of dS)."""
+    from sparse_top_attention_topk_amd import _lib
+    p = wl.make_problem("dsv4_flash_h128")
+    say(f"[gpu] bwd from o, full size: T={p.T} H={p.H} W={p.W}")
+    d = {k: None if v is None else v.to(DEV) for k, v in
+         dict(q=p.q, kv=p.kv, dO=p.dO, idx=p.topk_idxs, length=p.topk_length, sink=p.attn_sink).items()}
+    o, lse = _lib.smla_fwd(d["q"], d["kv"], d["idx"], d["length"], d["sink"], p.scale)
+    delta = _lib.smla_bwd_preprocess(o, d["dO"])
+    dq2, dkv2, ds2 = _lib.smla_bwd(d["q"], d["kv"], d["dO"], lse, delta, d["idx"], d["length"], d["sink"],
+                                   p.scale)
+    dq1, dkv1, ds1, delta1 = _lib.smla_bwd_from_o(d["q"], d["kv"], d["dO"], o, lse, d["idx"], d["length"],
+                                                  d["sink"], p.scale)
+    torch.cuda.synchronize()
+    m = delta.abs().max().item()
+    e = (delta1 - delta).abs().max().item()
+    say(f"[gpu] bwd from o, full size: delta max diff {e:.3e} (max {m:.3e})")
+    assert torch.isfinite(delta1).all() and e <= 1e-5 * m + 1e-7
+    for name, a, b in (("dq", dq1.float(), dq2.float()), ("dkv", dkv1, dkv2), ("d_sink", ds1, ds2)):
+        mb = b.abs().max().item()
+        err = (a - b).abs().max().item()
+        cos = torch.nn.functional.cosine_similarity(a.flatten().double(), b.flatten().double(), dim=0).item()
+        say(f"[gpu] bwd from o, full size: {name} max diff {err:.3e} (max {mb:.3e}), cos {cos:.8f}")
+        assert torch.isfinite(a).all() and err <= 2e-2 * mb and cos >= 0.9995, name
 
 
 def test_exact_delta_full_size_sampled():
