@@ -28,6 +28,8 @@
 #include "kv_tile.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace smla {
 
 // A head's reference max is fixed at its first valid block and O is never
@@ -62,39 +64,52 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
     static_assert(NW == 4, "the gather schedule assumes 16 main rows and 2 rope loads per wave");
     const int gids = Tile::template row_ids<NW>(grows, wave, lane);
 
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        // S^T for slots 32 half .. +31; K operands two k-steps ahead
-        f32x4 sacc[2][NT];
+    // The block's two halves in the order S(0), S(1), PV(0), PV(1): the
+    // exponentials of half 0 run between the MFMAs of S(1) and those of half
+    // 1 between the MFMAs of PV(0), so the softmax's VALU work overlaps the
+    // matrix work instead of leaving the MFMA pipe idle.  Each half's
+    // arithmetic and its order are unchanged.
+    f32x4 sacc[2][2][NT];                       // [half][m][nt]
+    bf16x8 pop[2][NT];
+    float psum[2][NT], m_use[2][NT];
+
+    // S^T for slots 32 h .. +31 (K operands two k-steps ahead); step(ks)
+    // runs after each k-step's MFMAs
+    auto s_loop = [&](auto H, auto&& step) {
+        constexpr int h = decltype(H)::value;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = zero4();
+            for (int nt = 0; nt < NT; ++nt) sacc[h][m][nt] = zero4();
         constexpr int KD = 3;
         bf16x8 kop[KD][2];
 #pragma unroll
         for (int i = 0; i < KD - 1; ++i)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) kop[i][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, i);
+            for (int m = 0; m < 2; ++m) kop[i][m] = Tile::row_op(tile, TL, (2 * h + m) * 16, i);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const int cur = ks % KD;
             if (ks + KD - 1 < C::KS) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    kop[(ks + KD - 1) % KD][m] = Tile::row_op(tile, TL, (2 * half + m) * 16, ks + KD - 1);
+                    kop[(ks + KD - 1) % KD][m] = Tile::row_op(tile, TL, (2 * h + m) * 16, ks + KD - 1);
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) sacc[m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[m][nt]);
-            // the next block's gather, spread over the first half's matrix work
-            if (half == 0 && ks < 16) Tile::template gather_main_row<NW>(gtile, gids, kvr, wave, lane, ks);
-            if (half == 0 && ks >= 16) Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, ks - 16);
+                for (int nt = 0; nt < NT; ++nt)
+                    sacc[h][m][nt] = mfma16(kop[cur][m], qop[nt][ks], sacc[h][m][nt]);
+            step(ks);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
 
-        // mask invalid slots before the exponential; log2-domain scores
+    // mask invalid slots before the exponential; log2-domain scores; the
+    // reference max of heads that have none yet (all lanes of a head agree
+    // after the reduction)
+    auto prep = [&](auto H) {
+        constexpr int h = decltype(H)::value;
         float hmax[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) hmax[nt] = -INFINITY;
@@ -102,17 +117,15 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
         for (int m = 0; m < 2; ++m) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
+                const bool ok = rows[(2 * h + m) * 16 + 4 * g + i] >= 0;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const float sv = ok ? sacc[m][nt][i] * a.scale_log2 : -INFINITY;
-                    sacc[m][nt][i] = sv;
+                    const float sv = ok ? sacc[h][m][nt][i] * a.scale_log2 : -INFINITY;
+                    sacc[h][m][nt][i] = sv;
                     hmax[nt] = fmaxf(hmax[nt], sv);
                 }
             }
         }
-        // heads without a reference yet take this half's max (all lanes of a
-        // head agree after the reduction)
         bool unset = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -126,21 +139,32 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
                 if (m_ref[nt] == -INFINITY) m_ref[nt] = hm;
             }
         }
-        bf16x8 pop[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float m_use = (m_ref[nt] == -INFINITY) ? 0.f : m_ref[nt];
-            float psum = 0.f;
+            m_use[h][nt] = (m_ref[nt] == -INFINITY) ? 0.f : m_ref[nt];
+            psum[h][nt] = 0.f;
+        }
+    };
+
+    // P = 2^(s - m_ref) for value k (0..7) of every head tile of half h
+    auto exp_step = [&](auto H, int k) {
+        constexpr int h = decltype(H)::value;
+        const int m = k >> 2, i = k & 3;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+        for (int nt = 0; nt < NT; ++nt) {
+            const float p = fast_exp2(sacc[h][m][nt][i] - m_use[h][nt]);
+            sacc[h][m][nt][i] = p;
+            psum[h][nt] += p;
+        }
+    };
+
+    // bf16 P as the B operand; the running sums
+    auto finish = [&](auto H) {
+        constexpr int h = decltype(H)::value;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(sacc[m][nt][i] - m_use);
-                    sacc[m][nt][i] = p;
-                    psum += p;
-                }
-            l_run[nt] += psum;
-            pop[nt] = cvt8(sacc[0][nt], sacc[1][nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+            l_run[nt] += psum[h][nt];
+            pop[h][nt] = cvt8(sacc[h][0][nt], sacc[h][1][nt]);
             // the sum of the bf16 weights the MFMA actually uses: O is
             // normalised by it, so O stays an exact convex combination of the
             // gathered V rows (a near one-hot row reproduces its V row)
@@ -148,24 +172,50 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
             float rsum = l_rnd[nt];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[nt][2 * j], pop[nt][2 * j + 1]}, one, rsum, false);
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[h][nt][2 * j], pop[h][nt][2 * j + 1]}, one,
+                                                       rsum, false);
             l_rnd[nt] = rsum;
         }
+    };
 
-        // O^T += V^T P^T over slots 32 half .. +31, V^T three column tiles ahead
+    // O^T += V^T P^T over slots 32 h .. +31, V^T three column tiles ahead;
+    // step(mc) runs after each column tile's MFMAs
+    auto pv_loop = [&](auto H, auto&& step) {
+        constexpr int h = decltype(H)::value;
         constexpr int VD = 4;
         bf16x8 vop[VD];
 #pragma unroll
-        for (int i = 0; i < VD - 1; ++i) vop[i] = Tile::slot_op(tile, TL, 32 * half, i);
+        for (int i = 0; i < VD - 1; ++i) vop[i] = Tile::slot_op(tile, TL, 32 * h, i);
 #pragma unroll
         for (int mc = 0; mc < C::MC; ++mc) {
             const int cur = mc % VD;
-            if (mc + VD - 1 < C::MC) vop[(mc + VD - 1) % VD] = Tile::slot_op(tile, TL, 32 * half, mc + VD - 1);
+            if (mc + VD - 1 < C::MC) vop[(mc + VD - 1) % VD] = Tile::slot_op(tile, TL, 32 * h, mc + VD - 1);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = mfma16(vop[cur], pop[nt], oacc[mc][nt]);
+            for (int nt = 0; nt < NT; ++nt) oacc[mc][nt] = mfma16(vop[cur], pop[h][nt], oacc[mc][nt]);
+            step(mc);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    // S(0), issuing the next block's gather: one main row per k-step, then
+    // the rope rows
+    s_loop(H0{}, [&](int ks) {
+        if (ks < 16) Tile::template gather_main_row<NW>(gtile, gids, kvr, wave, lane, ks);
+        else Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, ks - 16);
+    });
+    prep(H0{});
+    s_loop(H1{}, [&](int ks) {
+        if (ks < 8) exp_step(H0{}, ks);
+    });
+    finish(H0{});
+    prep(H1{});
+    pv_loop(H0{}, [&](int mc) {
+        if (mc < 8) exp_step(H1{}, mc);
+    });
+    finish(H1{});
+    pv_loop(H1{}, [](int) {});
 }
 
 // topk_idxs[t][j] for any j (clamped into the row so the read is in bounds);
