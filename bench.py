@@ -1,7 +1,9 @@
 """Benchmark: sparse MLA forward + backward on one MI355X.
 
 One step = smla_fwd + smla_bwd_preprocess + smla_bwd over one batch of the
-synthetic workload (inputs already resident in HBM).  Default workload:
+synthetic workload (inputs already resident in HBM).  ``value`` comes from the
+wall clock around the timed steps (plain calls); the per-stage times in
+``detail`` from a few more steps with HIP events at the stage boundaries.  Default workload:
 DeepSeek-V4-like H=128, T = S_kv = 4096 causal, d_qk = 576 (512 latent + 64
 rope), d_v = 512, window 128 + top-k 512 slots per token, -1 padded,
 non-compact, fp32 sink.
@@ -119,13 +121,19 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [new_events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # the timed steps: plain calls (no events between the kernels)
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # per-stage times: the same steps again with events at the stage boundaries
+    evs = [new_events() for _ in range(min(args.steps, 5))]
+    torch.cuda.synchronize()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
 
     # the high-accuracy Delta (smla_bwd_delta_exact, in place of the
     # preprocess): timed on its own after the steps, not part of `value`
