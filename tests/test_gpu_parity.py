@@ -175,6 +175,8 @@ FROM_O_CASES = {
     "edge-sink-h64": lambda: wl.make_edge_sink(64),
     "width-118-h128": lambda: wl.make_edge_width118(128),
     "batched": lambda: wl.make_batched(),
+    "dsv4-512-h128": lambda: wl.make_dsv4(320, 128, 512, 512, 96, seed=71, window=64),
+    "dsv4-512-h64-compact": lambda: wl.make_dsv4(320, 64, 512, 512, 96, seed=72, window=64, compact=True),
 }
 
 
