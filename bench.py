@@ -13,7 +13,7 @@ FLOP convention of the pages ([flash-attn #2882] Performance): forward
 2.5x the forward.  Gathered bytes (the pages' TB/s model): gathered KV rows
 (K * d_qk * 2 bytes per token) + Q read + O write.
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: the library runs on
 one GPU.
 """
 from __future__ import annotations
@@ -70,7 +70,7 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+        print(f"bench.py: --gpus {args.gpus} requested; the library runs on one GPU only "
               "(no collectives, no sharding).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

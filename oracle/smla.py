@@ -19,7 +19,7 @@ token's valid top-k slots, with an optional per-head sink logit that joins the
 softmax denominator and carries no value row.  Query heads share one latent KV
 row set (MQA): K = kv[:, :d_qk], V = kv[:, :d_v].
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 
 * the forward returns the sink-free natural-log LSE of the valid scores;
   O carries the sink's normalisation (the backward folds the sink into the LSE
