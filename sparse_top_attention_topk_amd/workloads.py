@@ -26,7 +26,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Problem", "make_problem", "make_batched", "segment", "PROBLEMS", "EDGE_HEADS"]
+__all__ = ["Problem", "make_problem", "make_batched", "make_degenerate", "segment", "PROBLEMS",
+           "EDGE_HEADS", "DEGENERATE_KINDS"]
 
 EDGE_HEADS = (1, 24, 64, 96, 128)
 
@@ -183,6 +184,54 @@ def make_edge_width118(H, seed=40, T=64, S=128):
         idx[t, pos] = rng.choice(S, size=100, replace=False)
     return Problem(f"edge_w118_h{H}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
                    torch.from_numpy(idx), None, s, meta=dict(seed=seed))
+
+
+DEGENERATE_KINDS = ("single", "all_invalid", "out_of_range", "duplicates")
+
+
+def make_degenerate(kind, seed=80):
+    """Small problems at the edges of the argument contract, with a sink.
+
+    single        T = S_kv = H = W = 1, d_qk = d_v = 512: one token whose one
+                  slot names the one KV row
+    all_invalid   T = 5, S_kv = 8, H = 3, width 70 (a full and a 6-slot
+                  block), every slot -1: every row is empty
+    out_of_range  T = 16, S_kv = 40, H = 8, width 96: per row 20 distinct
+                  valid indices, 20 indices in [S_kv, S_kv + 1000), 20 below -1
+                  and -1 elsewhere, at random positions (only the valid ones
+                  name a row)
+    duplicates    T = 16, S_kv = 50, H = 8, width 64: per row 40 slots drawn
+                  with replacement from [0, 50) (so rows repeat), -1 after;
+                  a row named twice by one token counts twice, as the
+                  slot-wise definition gives
+    """
+    rng = np.random.default_rng(seed + DEGENERATE_KINDS.index(kind))
+    if kind == "single":
+        T, S, H, dqk, dv, W = 1, 1, 1, 512, 512, 1
+        q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+        idx = np.zeros((T, W), dtype=np.int32)
+    elif kind == "all_invalid":
+        T, S, H, dqk, dv, W = 5, 8, 3, 576, 512, 70
+        q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+        idx = np.full((T, W), -1, dtype=np.int32)
+    elif kind == "out_of_range":
+        T, S, H, dqk, dv, W = 16, 40, 8, 576, 512, 96
+        q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+        idx = np.full((T, W), -1, dtype=np.int32)
+        for t in range(T):
+            pos = rng.permutation(W)
+            idx[t, pos[:20]] = rng.choice(S, size=20, replace=False)
+            idx[t, pos[20:40]] = rng.integers(S, S + 1000, size=20)
+            idx[t, pos[40:60]] = rng.integers(-(2 ** 31), -1, size=20)
+    elif kind == "duplicates":
+        T, S, H, dqk, dv, W = 16, 50, 8, 576, 512, 64
+        q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+        idx = np.full((T, W), -1, dtype=np.int32)
+        idx[:, :40] = rng.integers(0, S, size=(T, 40))
+    else:
+        raise ValueError(f"unknown degenerate problem {kind!r}")
+    return Problem(f"degenerate_{kind}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), None, s, meta=dict(seed=seed, kind=kind))
 
 
 SATURATING_SINKS = (3.0e38, -3.0e38, float("inf"), float("-inf"))

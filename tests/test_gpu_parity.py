@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from parity import (compare_full, compare_exact_delta, run_gpu, run_gpu_exact, run_gpu_from_o, run_oracle,
-                    oracle_delta_exact, say, check_tensor, check_lse, referenced_rows,
+                    oracle_delta_exact, say, check_tensor, check_lse, check_dkv_rows, referenced_rows,
                     tokens_referencing)
 from sparse_top_attention_topk_amd import workloads as wl
 
@@ -78,6 +78,54 @@ def test_edge_saturating_sinks(H):
 def test_width_118_tail(H):
     """Non-compact width 118 = 100 valid + 18 padding: a partial last block."""
     _run_and_compare(wl.make_edge_width118(H), f"width-118-h{H}")
+
+
+@pytest.mark.parametrize("kind", wl.DEGENERATE_KINDS)
+def test_degenerate_problems(kind):
+    """Edges of the argument contract: one token with one slot over a one-row
+    KV; every slot -1; indices >= S_kv and below -1 among valid ones; KV rows
+    named more than once by one token (each naming counts).
+
+    O, LSE, dQ and dKV meet the usual bars.  d_sink is checked through the
+    exact Delta against the fp64 oracle (bar 1e-4): with 16 tokens whose
+    Delta terms cancel, rounding O to bf16 alone moves the oracle's own
+    d_sink by up to 0.9 % of its largest head, which leaves the 1e-2 bar of
+    the bf16-O Delta no room for the kernels' rounding.  The default path's
+    d_sink must still be -sum_t p_sink Delta of its own LSE and Delta."""
+    p = wl.make_degenerate(kind)
+    say(f"[gpu] case degenerate-{kind}: T={p.T} S_kv={p.S_kv} H={p.H} d_qk={p.d_qk} W={p.W}")
+    gpu = run_gpu(p, DEV)
+    ref = run_oracle(p)
+    errors = []
+    check_tensor("o", gpu["o"], ref["o"], errors)
+    check_lse(gpu["lse"], ref["lse"], errors)
+    check_tensor("dq", gpu["dq"], ref["dq"], errors)
+    check_tensor("dkv", gpu["dkv"], ref["dkv"], errors)
+    check_dkv_rows(gpu["dkv"], ref["dkv"], errors)
+    # default path: d_sink from its own LSE and Delta (fp64 on the host)
+    lse, dl = gpu["lse"].astype(np.float64), gpu["delta"].astype(np.float64)
+    sk = p.attn_sink.double().numpy()[None, :]
+    ps = np.where(np.isneginf(lse), 0.0, 1.0 / (1.0 + np.exp(-(sk - np.where(np.isneginf(lse), 0.0, lse)))))
+    own = -(ps * dl).sum(axis=0)
+    scale_h = np.abs(ps * dl).sum(axis=0)         # fp32 summation error is relative to this
+    if np.any(np.abs(gpu["d_sink"] - own) > 1e-5 * scale_h + 1e-7):
+        errors.append(f"d_sink: {gpu['d_sink']} vs its own -sum p_sink Delta {own}")
+    # exact-Delta path against the fp64 oracle
+    ge = run_gpu_exact(p, DEV)
+    ref64 = run_oracle(p, delta_from="fp64")
+    ms = np.abs(ref64["d_sink"]).max()
+    es = np.abs(ge["d_sink"] - ref64["d_sink"]).max()
+    say(f"[gpu] degenerate-{kind}: exact-Delta d_sink max err {es:.3e} vs max {ms:.3e}")
+    if es > EXACT_TOL * ms + 1e-7:
+        errors.append(f"exact-Delta d_sink: max err {es:.3e} vs max {ms:.3e}")
+    assert not errors, f"degenerate-{kind}: " + "; ".join(errors)
+    if kind == "all_invalid":
+        assert np.all(gpu["o"] == 0) and np.all(np.isneginf(gpu["lse"]))
+        assert np.all(gpu["dq"] == 0) and np.all(gpu["dkv"] == 0) and np.all(gpu["d_sink"] == 0)
+    if kind == "out_of_range":
+        assert np.all(gpu["dkv"][~referenced_rows(p)] == 0)
+    if kind == "single":
+        assert np.all(np.isfinite(gpu["lse"])) and np.any(gpu["dkv"] != 0)
 
 
 def test_nan_prefilled_outputs_fully_written_and_deterministic():

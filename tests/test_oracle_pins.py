@@ -354,6 +354,54 @@ def test_columns_past_skv_still_receive_dkv():
     assert all(np.any(dkv[r] != 0) for r in late)
 
 
+def test_duplicate_slots_equal_copied_kv_rows():
+    """By the slot-wise definition a KV row named twice by one token counts
+    twice.  The same problem with each second naming pointed at an appended
+    copy of the row has distinct indices; its outputs must match, with the
+    copy's dKV added back to the row.  This ties the duplicate branch of the
+    dKV scatter to the distinct one."""
+    rng = np.random.default_rng(91)
+    T, S, H, d_qk, d_v, W = 5, 6, 3, 8, 4, 6
+    q = rng.standard_normal((T, H, d_qk))
+    kv = rng.standard_normal((S, d_qk))
+    dO = rng.standard_normal((T, H, d_v))
+    idx = np.array([[2, 2, 0, -1, 3, 2],
+                    [1, 4, 1, -1, -1, -1],
+                    [-1, -1, -1, -1, -1, -1],
+                    [5, 0, 5, 0, 5, 0],
+                    [3, -1, 1, 2, 4, 0]], dtype=np.int32)
+    sink = rng.standard_normal(H)
+    dup = dict(q=q, kv=kv, dO=dO, topk_idxs=idx, topk_length=None, attn_sink=sink,
+               scale=0.35, d_v=d_v)
+    kv2, idx2, origin = [kv], idx.copy(), []
+    for t in range(T):
+        seen = set()
+        for j in range(W):
+            r = int(idx[t, j])
+            if r < 0:
+                continue
+            if r in seen:
+                idx2[t, j] = S + len(origin)
+                origin.append(r)
+                kv2.append(kv[r:r + 1])
+            seen.add(r)
+    assert origin, "the problem must hold duplicates"
+    dist = dict(dup, kv=np.concatenate(kv2), topk_idxs=idx2)
+    O1, l1, _ = run_fwd(dup)
+    O2, l2, _ = run_fwd(dist)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isfinite(l1), np.isfinite(l2))
+    np.testing.assert_allclose(l1[np.isfinite(l1)], l2[np.isfinite(l2)], rtol=0, atol=1e-12)
+    dq1, dkv1, ds1, _ = run_bwd(dup)
+    dq2, dkv2, ds2, _ = run_bwd(dist)
+    folded = dkv2[:S].copy()
+    for k, r in enumerate(origin):
+        folded[r] += dkv2[S + k]
+    np.testing.assert_allclose(dq1, dq2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dkv1, folded, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ds1, ds2, rtol=0, atol=1e-12)
+
+
 def test_layout_and_slot_permutation_invariance():
     p = small_problem(19, layout="noncompact")
     T, W = p["topk_idxs"].shape

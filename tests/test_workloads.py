@@ -106,3 +106,17 @@ def test_edge_sink_anti_aligned_rows_have_very_negative_lse():
     _, lse, _ = oracle.oracle_fwd(x["q"], x["kv"], x["topk_idxs"], None, None, x["scale"],
                                   x["d_v"], tokens=toks)
     assert lse.max() < -80
+
+
+def test_degenerate_problems_have_their_stated_structure():
+    p = wl.make_degenerate("single")
+    assert (p.T, p.S_kv, p.H, p.W, p.d_qk) == (1, 1, 1, 1, 512) and p.valid_count() == 1
+    p = wl.make_degenerate("all_invalid")
+    assert p.valid_count() == 0 and p.W == 70 and (p.topk_idxs.numpy() == -1).all()
+    p = wl.make_degenerate("out_of_range")
+    idx = p.topk_idxs.numpy()
+    assert ((idx >= p.S_kv).sum(axis=1) == 20).all() and ((idx < -1).sum(axis=1) == 20).all()
+    assert p.valid_count() == 20 * p.T
+    p = wl.make_degenerate("duplicates")
+    idx = p.topk_idxs.numpy()
+    assert all(len(set(r[r >= 0].tolist())) < (r >= 0).sum() for r in idx)
