@@ -35,7 +35,9 @@
 //                valid slot names get 0)
 //   dsink        one workgroup per head: sum over tokens in token order
 // No fp32 atomics touch dkv: the scatter is a write of per-slot partials plus
-// a streaming reduce.  An empty row (no valid slot) is a uniform branch: dQ = 0
+// a streaming reduce.  A 64-slot block without a valid slot (the tail of a
+// non-compact row) runs no math in bwd_sdp, bwd_dq and bwd_dkv, and its P and
+// dS are never stored or read: it would add exact zeros.  An empty row (no valid slot) is a uniform branch: dQ = 0
 // is written and the token's q, dO, lse and delta are not read.
 #include "kv_tile.h"
 #include "launch.h"
@@ -209,7 +211,7 @@ __device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
 }
 
 // The double-buffered gather loop of the kernels that gather KV tiles:
-// body(tile, rows, b, parity, gtile, grows) runs block b from tile 0 (even b,
+// body(tile, rows, b, parity, gs, live) runs block b from tile 0 (even b,
 // parity 0) or tile 1 (odd b, parity 1) and issues, spread over its math
 // (GatherSpread), this wave's share of the gather of block b + 1 from the
 // slot rows grows into the other tile gtile.  After the last block that
@@ -253,7 +255,7 @@ struct NoPost {
 
 template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
-                                                int (*s_rows)[BLK], int t, int L, int nblk,
+                                                int (*s_rows)[BLK], int* s_live, int t, int L, int nblk,
                                                 int wave, int lane, Body&& body, Pre&& pre = Pre{},
                                                 Post&& post = Post{}) {
     using Tile = KvTileSwz<DQK>;
@@ -262,8 +264,8 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
     if (tid < BLK) {
-        s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
-        s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
+        put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, L, a.S_kv, tid), tid);
+        put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid), tid);
     }
     __syncthreads();
     if (nblk > 0) {
@@ -280,21 +282,25 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         if (b > 0 && b + 1 < nblk && tid < BLK)
-            s_rows[(b + 1) % 3][tid] = valid_row_b(ahead, (b + 1) * BLK + tid, L, a.S_kv);
+            put_rows(s_rows[(b + 1) % 3], &s_live[(b + 1) % 3], valid_row_b(ahead, (b + 1) * BLK + tid, L, a.S_kv),
+                     tid);
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 1 < nblk) pre(b + 1, P1{});
-        body(s_tile0, s_rows[b % 3], b, P0{}, GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane));
+        body(s_tile0, s_rows[b % 3], b, P0{}, GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane),
+             __builtin_amdgcn_readfirstlane(s_live[b % 3]) != 0);
         if (b + 1 >= nblk) break;
         wait_vmem();
         if (b + 2 < nblk && tid < BLK)
-            s_rows[(b + 2) % 3][tid] = valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv);
+            put_rows(s_rows[(b + 2) % 3], &s_live[(b + 2) % 3], valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv),
+                     tid);
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 2 < nblk) pre(b + 2, P0{});
-        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{}, GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane));
+        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{}, GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane),
+             __builtin_amdgcn_readfirstlane(s_live[(b + 1) % 3]) != 0);
     }
     wait_vmem();                 // the spare gather after the last block
 }
@@ -423,6 +429,7 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
+    __shared__ int s_live[3];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -488,9 +495,9 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
     const typename Tile::Lane TL = Tile::lane_bases(lane);
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs) {
-                                 if (active)
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, t, L, nblk, wave, lane,
+                             [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
+                                 if (active && live)
                                      sdp_block<DQK, NW, NT, EXACT>(a, tile, TL, rows, qop, dop, lse2, dlt,
                                                                    pdp, t, h_wave, b, lane, gs);
                                  else
@@ -536,6 +543,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
+    __shared__ int s_live[3];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -593,11 +601,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, t, L, nblk, wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs) {
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, t, L, nblk, wave, lane,
+                             [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs, bool live) {
         (void)rows;
         (void)b;
-        if (!active) {
+        if (!active || !live) {
             gs.all();
             return;
         }
@@ -747,6 +755,12 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
                                           __amdgpu_buffer_rsrc_t prs, int voff, int ntc, int lane) {
     constexpr int HP = 32 * HK;
     const int g = lane >> 4, n = lane & 15;
+    {
+        // a block without a valid slot writes nothing (and its P / dS tile
+        // was never stored): skip it
+        const int v = raw[lane];
+        if (__builtin_amdgcn_ballot_w64(b * BLK + lane < L && v >= 0 && v < a.S_kv) == 0) return;
+    }
     // four quarters of 16 slots: one accumulator tile per column tile
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {

@@ -108,6 +108,15 @@ __device__ __forceinline__ void stage_slot_idx(int* dst, const int32_t* idx, int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 4, (b * 64 + lane) * 4, 0, 0, 0);
 }
 
+// Store the KV rows of one block's 64 slots (a whole wave: lane = slot; -1
+// for a slot that is not valid) and whether any of them is valid.  A block
+// with no valid slot adds exact zeros to every sum, so its math is skipped.
+__device__ __forceinline__ void put_rows(int* rows, int* live, int r, int lane) {
+    rows[lane] = r;
+    const bool any = __builtin_amdgcn_ballot_w64(r >= 0) != 0;
+    if (lane == 0) *live = any;
+}
+
 // Block storage of fp32 values in 16 bits each (the dKV partials): a group of
 // four values keeps the largest fp32 exponent field E among them (8 bits) and
 // each value as a 14-bit signed multiple of 2^(E - 139), i.e. of 2^-12 times

@@ -3,6 +3,11 @@
 // Method ([flash-attn #2882] Agent Notes; [cuDNN-FE #785] Summary 2-3): for
 // each token, the H query heads share the token's gathered KV rows.  Per block
 // of 64 top-k slots the workgroup
+//   0. (once) finds the row's last valid slot: the blocks after its block
+//      hold only padding (the tail of a non-compact row) and are not run,
+//      as a compact row's length bounds its block count ([cuDNN-FE #785]
+//      Summary 2); a block without a valid slot adds exact zeros everywhere,
+//      so the output is the same bits;
 //   1. resolves slot -> KV row (invalid slots -> -1) two blocks ahead;
 //   2. gathers the rows of the NEXT block into the other of two LDS tiles with
 //      asynchronous direct global->LDS 16-byte loads, so that the gather of
@@ -236,6 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
+    __shared__ int s_last[NW];
     __shared__ int s_rerun;
     static_assert(64 * C::DV <= Tile::ELEMS && C::HT <= 128, "O staging must fit in the tiles");
 
@@ -248,7 +254,6 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     const int h_wave = h_wg + wave * NT * 16;
     const bool active = h_wave < a.H;                 // wave-uniform
     const int L = row_length(a.len, t, a.W);
-    const int nblk = (L + BLK - 1) / BLK;
 
     if (tid == 0) s_rerun = 0;
 
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int head = h_wave + nt * 16 + n;
-        const bool hv = head < a.H && nblk > 0;
+        const bool hv = head < a.H && L > 0;
         const __bf16* qp = a.q + ((size_t)t * a.H + (hv ? head : 0)) * DQK + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qop[nt][ks] = hv ? ld8(qp + 32 * ks) : zero8();
@@ -268,6 +273,27 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     float m_ref[NT], rmax[NT], l_run[NT], l_rnd[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) m_ref[nt] = -INFINITY;
+
+    // The row's last valid slot: the blocks after its block hold padding only
+    // (the tail of a non-compact row), so the block loop ends there.  Each
+    // wave's maximum goes to s_last, read after the first barrier below.
+    {
+        int last = -1;
+        for (int j0 = 0; j0 < L; j0 += 4 * NTH) {
+            int v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = raw_index(a, t, j0 + k * NTH + tid);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k * NTH + tid;
+                if (valid_row(v[k], j, L, a.S_kv) >= 0) last = j;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m, 64));
+        if (lane == 0) s_last[wave] = last;
+    }
+    int nblk = 0;
 
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -282,6 +308,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
         }
         __syncthreads();
+        if (pass == 0) {
+            int last = s_last[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
+            nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1);
+        }
         if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
 
         // Two blocks per iteration so that each tile is a distinct LDS object.
