@@ -255,7 +255,7 @@ struct NoPost {
 
 template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
-                                                int (*s_rows)[BLK], int* s_live, int t, int L, int nblk,
+                                                int (*s_rows)[BLK], int* s_live, int* s_last, int t, int L, int nblk,
                                                 int wave, int lane, Body&& body, Pre&& pre = Pre{},
                                                 Post&& post = Post{}) {
     using Tile = KvTileSwz<DQK>;
@@ -263,14 +263,41 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     using P1 = std::integral_constant<int, 1>;
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
+    // The row's last valid slot: the blocks after its block hold padding only
+    // (the tail of a non-compact row) and are not run.  Its loads go out with
+    // those of the first slot rows.
+    {
+        constexpr int NTH = NW * 64;
+        int last = -1;
+        for (int j0 = 0; j0 < L; j0 += 4 * NTH) {
+            int v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = raw_index_b(a, t, j0 + k * NTH + tid);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k * NTH + tid;
+                if (valid_row_b(v[k], j, L, a.S_kv) >= 0) last = j;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m, 64));
+        if (lane == 0) s_last[wave] = last;
+    }
     if (tid < BLK) {
         put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, L, a.S_kv, tid), tid);
         put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid), tid);
     }
     __syncthreads();
-    if (nblk > 0) {
-        pre(0, P0{});
-        Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+    int last = s_last[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
+    const int nbr = nblk;                                   // blocks of the row
+    nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1);
+    if (nbr > 0) {
+        if (nblk > 0) {
+            pre(0, P0{});
+            Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+        }
         post();
     }
     // Block k: wait for its tile; store the slot rows of block k + 1 (their
@@ -430,6 +457,7 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
     __shared__ int s_live[3];
+    __shared__ int s_last[NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -495,7 +523,7 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
     const typename Tile::Lane TL = Tile::lane_bases(lane);
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, t, L, nblk, wave, lane,
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, wave, lane,
                              [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
                                  if (active && live)
                                      sdp_block<DQK, NW, NT, EXACT>(a, tile, TL, rows, qop, dop, lse2, dlt,
@@ -544,6 +572,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
     __shared__ int s_rows[3][BLK];
     __shared__ int s_live[3];
+    __shared__ int s_last[NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -601,7 +630,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, t, L, nblk, wave, lane,
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, wave, lane,
                              [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs, bool live) {
         (void)rows;
         (void)b;
