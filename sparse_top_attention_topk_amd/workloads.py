@@ -26,8 +26,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Problem", "make_problem", "make_batched", "make_degenerate", "segment", "PROBLEMS",
-           "EDGE_HEADS", "DEGENERATE_KINDS"]
+__all__ = ["Problem", "make_problem", "make_batched", "make_degenerate", "make_block_gaps",
+           "pack_live_blocks", "segment", "PROBLEMS", "EDGE_HEADS", "DEGENERATE_KINDS"]
 
 EDGE_HEADS = (1, 24, 64, 96, 128)
 
@@ -232,6 +232,44 @@ def make_degenerate(kind, seed=80):
         raise ValueError(f"unknown degenerate problem {kind!r}")
     return Problem(f"degenerate_{kind}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
                    torch.from_numpy(idx), None, s, meta=dict(seed=seed, kind=kind))
+
+
+def make_block_gaps(H=64, seed=90, T=96, S=200, nblocks=8):
+    """Non-compact rows of nblocks 64-slot blocks, each block either all -1
+    or live: per token a random set of 0..4 live blocks anywhere in the row
+    (so whole blocks of padding sit before, between and after them), each
+    live block with 1..64 valid slots at random positions (-1 elsewhere);
+    a token's indices are distinct."""
+    rng = np.random.default_rng(seed)
+    dqk, dv, W = 576, 512, 64 * nblocks
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        live = rng.choice(nblocks, size=int(rng.integers(0, 5)), replace=False)
+        cnt = [int(rng.integers(1, 65)) for _ in live]
+        rows = rng.choice(S, size=sum(cnt), replace=False)
+        k = 0
+        for b, c in zip(live, cnt):
+            pos = 64 * int(b) + rng.choice(64, size=c, replace=False)
+            idx[t, pos] = rows[k:k + c]
+            k += c
+    return Problem(f"block_gaps_h{H}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), None, s, meta=dict(seed=seed))
+
+
+def pack_live_blocks(p):
+    """The same problem with each token's blocks that hold a valid slot moved,
+    in order and unchanged, to the front of its row (the rest all -1)."""
+    idx = p.topk_idxs.numpy()
+    T, W = idx.shape
+    out = np.full_like(idx, -1)
+    for t in range(T):
+        blocks = [idx[t, j:j + 64] for j in range(0, W, 64)]
+        live = [b for b in blocks if ((b >= 0) & (b < p.S_kv)).any()]
+        for i, b in enumerate(live):
+            out[t, 64 * i: 64 * i + b.size] = b
+    return Problem(p.name + "_packed", p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale, p.q, p.kv, p.dO,
+                   torch.from_numpy(out), None, p.attn_sink, meta=dict(p.meta, packed=True))
 
 
 SATURATING_SINKS = (3.0e38, -3.0e38, float("inf"), float("-inf"))

@@ -128,6 +128,20 @@ def test_degenerate_problems(kind):
         assert np.all(np.isfinite(gpu["lse"])) and np.any(gpu["dkv"] != 0)
 
 
+@pytest.mark.parametrize("H", (64, 128))
+def test_blocks_without_valid_slots_change_no_bit(H):
+    """64-slot blocks holding no valid slot, before, between and after the
+    live ones, are skipped; they would add exact zeros.  Moving each token's
+    live blocks to the front of its row (the same blocks, in order) gives the
+    same bits for every output, and the gapped problem meets the oracle."""
+    p = wl.make_block_gaps(H)
+    _run_and_compare(p, f"block-gaps-h{H}")
+    a = run_gpu(p, DEV)
+    b = run_gpu(wl.pack_live_blocks(p), DEV)
+    for k in ("o", "lse", "dq", "dkv", "delta", "d_sink"):
+        assert np.array_equal(a[k], b[k]), f"{k} differs between the gapped and packed rows"
+
+
 def test_nan_prefilled_outputs_fully_written_and_deterministic():
     p = wl.make_edge_compact(64)
     a = run_gpu(p, DEV, nan_prefill=True)

@@ -120,3 +120,21 @@ def test_degenerate_problems_have_their_stated_structure():
     p = wl.make_degenerate("duplicates")
     idx = p.topk_idxs.numpy()
     assert all(len(set(r[r >= 0].tolist())) < (r >= 0).sum() for r in idx)
+
+
+def test_block_gaps_structure_and_packing():
+    p = wl.make_block_gaps(64)
+    idx = p.topk_idxs.numpy()
+    blocks = idx.reshape(p.T, -1, 64)
+    live = (blocks >= 0).any(axis=2)
+    assert live.sum(axis=1).max() <= 4 and (live.sum(axis=1) == 0).any()
+    # some row has a dead block before one of its live blocks
+    assert any(live[t].any() and not live[t][: np.nonzero(live[t])[0][-1]].all() for t in range(p.T))
+    for t in range(p.T):
+        v = idx[t][idx[t] >= 0]
+        assert len(set(v.tolist())) == v.size
+    q = wl.pack_live_blocks(p)
+    qb = q.topk_idxs.numpy().reshape(p.T, -1, 64)
+    for t in range(p.T):
+        n = int(live[t].sum())
+        assert np.array_equal(qb[t, :n], blocks[t][live[t]]) and (qb[t, n:] == -1).all()
