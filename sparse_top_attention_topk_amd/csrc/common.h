@@ -126,26 +126,34 @@ __device__ __forceinline__ void put_rows(int* rows, int* live, int r, int lane) 
 // non-finite value decodes as NaN.  Layout: w0 = E | q0 << 8 | (q1 & 0x3FF)
 // << 22, w1 = q1 >> 10 | q2 << 4 | q3 << 18 (q in 14-bit two's complement).
 __device__ __forceinline__ u32x2 pack_blk4(f32x4 v) {
-    uint32_t e = 0;
+    // E: the largest exponent field, i.e. that of the largest magnitude bits
+    // (through scalars: a bit cast of a vector element can read the wrong
+    // element with this compiler)
+    uint32_t b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // (through a scalar: a bit cast of a vector element can read the
-        // wrong element with this compiler)
         const float x = v[i];
-        const uint32_t ei = (__builtin_bit_cast(uint32_t, x) >> 23) & 0xFFu;
-        e = ei > e ? ei : e;
+        b[i] = __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu;
     }
+    const uint32_t bm01 = b[0] > b[1] ? b[0] : b[1];
+    const uint32_t bm23 = b[2] > b[3] ? b[2] : b[3];
+    const uint32_t e = (bm01 > bm23 ? bm01 : bm23) >> 23;
     const float sc = __builtin_bit_cast(float, (266u - (e > 12u ? e : 13u)) << 23);   // 2^(139 - E)
     uint32_t q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        int qi = (int)__builtin_rintf(v[i] * sc);
+        // |v sc| < 2^13: adding 1.5 * 2^23 in one rounding leaves round-to-
+        // nearest-even(v sc) in the low bits, as rint(v sc) would
+        const float r = __builtin_fmaf(v[i], sc, 12582912.0f);
+        int qi = (int)(__builtin_bit_cast(uint32_t, r) - 0x4B400000u);
         qi = qi < -8191 ? -8191 : (qi > 8191 ? 8191 : qi);
         q[i] = (uint32_t)qi & 0x3FFFu;
     }
-    const u32x2 w = {e | (q[0] << 8) | (q[1] << 22), (q[1] >> 10) | (q[2] << 4) | (q[3] << 18)};
-    if (e == 255u) return u32x2{255u, 0u};
-    return e > 12u ? w : u32x2{0u, 0u};
+    const uint32_t w0 = e | (q[0] << 8) | (q[1] << 22);
+    const uint32_t w1 = (q[1] >> 10) | (q[2] << 4) | (q[3] << 18);
+    // selects, not a branch: small blocks store 0, non-finite ones {255, 0}
+    const bool keep = e > 12u, inf = e == 255u;
+    return u32x2{inf ? 255u : (keep ? w0 : 0u), keep && !inf ? w1 : 0u};
 }
 
 __device__ __forceinline__ f32x4 unpack_blk4(u32x2 w) {
