@@ -81,6 +81,9 @@ def main():
     n_valid = p.valid_count()
     fwd_flop = 2.0 * p.H * (p.d_qk + p.d_v) * n_valid
     bwd_flop = 2.5 * fwd_flop
+    # the pages' timing tables count K = slots per token (W for every token),
+    # valid or not: a second figure in that convention, for comparison only
+    fwd_flop_nominal = 2.0 * p.H * (p.d_qk + p.d_v) * p.T * p.W
     gathered = n_valid * p.d_qk * 2 + p.T * p.H * (p.d_qk + p.d_v) * 2
 
     q, kv, dO = p.q.to(dev), p.kv.to(dev), p.dO.to(dev)
@@ -195,6 +198,11 @@ def main():
             "fwd_mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
             "fwd_flop": fwd_flop, "bwd_flop": bwd_flop, "gathered_bytes_fwd": gathered,
+            "tflops_nominal_k": {
+                "fwd": round(fwd_flop_nominal / fwd_s / 1e12, 1),
+                "bwd": round(2.5 * fwd_flop_nominal / ((step_ms - stage_ms["fwd"]) * 1e-3) / 1e12, 1),
+                "step": round(3.5 * fwd_flop_nominal / (ms_per_step * 1e-3) / 1e12, 1),
+            },
             "delta_exact_us": round(delta_exact_ms * 1e3, 1),
             "step_us_exact_delta_mode": round((step_ms - stage_ms["preprocess"] + delta_exact_ms) * 1e3, 1),
         },
