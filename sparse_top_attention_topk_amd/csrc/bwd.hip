@@ -214,8 +214,8 @@ __device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
 // body(tile, rows, b, parity, gs, live) runs block b from tile 0 (even b,
 // parity 0) or tile 1 (odd b, parity 1) and issues, spread over its math
 // (GatherSpread), this wave's share of the gather of block b + 1 from the
-// slot rows grows into the other tile gtile.  After the last block that
-// gather loads rows nobody reads into a tile that is free.  pre(b, parity)
+// slot rows grows into the other tile gtile (the last block issues none).
+// pre(b, parity)
 // runs before block b - 1's body and may issue global loads for block b
 // (they complete before block b starts, and waiting for them never waits for
 // a gather issued after them).
@@ -235,16 +235,17 @@ struct GatherSpread {
     static constexpr int STEPS = RPW + (Tile::ROPE ? 8 / NW : 0);
     __bf16* gtile;
     const int* grows;
-    __amdgpu_buffer_rsrc_t kvr;
-    int ids, wave, lane;
-    __device__ GatherSpread(__bf16* gt, const int* gr, __amdgpu_buffer_rsrc_t rs, int w, int l)
-        : gtile(gt), grows(gr), kvr(rs), ids(Tile::template row_ids<NW>(gr, w, l)), wave(w), lane(l) {}
+    __amdgpu_buffer_rsrc_t kvr;      // zero records when there is no next block: no memory read
+    int ids, wave, lane, s_kv;
+    __device__ GatherSpread(__bf16* gt, const int* gr, const __bf16* kv, int w, int l, int S_kv, bool next)
+        : gtile(gt), grows(gr), kvr(Tile::kv_rsrc_if(kv, S_kv, next)),
+          ids(Tile::template row_ids<NW>(gr, w, l, S_kv)), wave(w), lane(l), s_kv(S_kv) {}
     // step is a compile-time constant after unrolling
     __device__ void step(int s) const {
         if (s < RPW) Tile::template gather_main_row<NW>(gtile, ids, kvr, wave, lane, s);
-        else if (s < STEPS) Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, s - RPW);
+        else if (s < STEPS) Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, s - RPW, s_kv);
     }
-    __device__ void all() const { Tile::template gather_async<NW>(gtile, grows, kvr, wave, lane); }
+    __device__ void all() const { Tile::template gather_async<NW>(gtile, grows, kvr, wave, lane, s_kv); }
 };
 
 // post() runs once, right after the first block's gather is issued: work that
@@ -286,6 +287,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     if (tid < BLK) {
         put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, L, a.S_kv, tid), tid);
         put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid), tid);
+        put_rows(s_rows[2], &s_live[2], -1, tid);        // written again before any block reads it
     }
     __syncthreads();
     int last = s_last[0];
@@ -296,7 +298,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     if (nbr > 0) {
         if (nblk > 0) {
             pre(0, P0{});
-            Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+            Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
         }
         post();
     }
@@ -315,7 +317,8 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 1 < nblk) pre(b + 1, P1{});
-        body(s_tile0, s_rows[b % 3], b, P0{}, GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane),
+        body(s_tile0, s_rows[b % 3], b, P0{},
+             GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane, a.S_kv, b + 1 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[b % 3]) != 0);
         if (b + 1 >= nblk) break;
         wait_vmem();
@@ -326,10 +329,11 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
         if (b + 2 < nblk) pre(b + 2, P0{});
-        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{}, GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane),
+        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{},
+             GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane, a.S_kv, b + 2 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[(b + 1) % 3]) != 0);
     }
-    wait_vmem();                 // the spare gather after the last block
+    wait_vmem();
 }
 
 // ---------------------------------------------------------------------------
@@ -920,7 +924,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             }
         }
     }
-    if (HP > a.H) zero_rows_past_h(s_pd1);   // the block loop's barrier orders it
+    // Every wave must be done reading the last staged piece before s_pd1's
+    // padded rows are cleared: with HK = 3 that piece lives in s_pd1.  The
+    // block loop's first barrier then orders the clearing before the reads.
+    if (HP > a.H) {
+        __syncthreads();
+        zero_rows_past_h(s_pd1);
+    }
 
     // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
     // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores

@@ -62,12 +62,14 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
                                           f32x4 (&oacc)[512 / 16][NT], float (&m_ref)[NT],
                                           float (&rmax)[NT], float (&l_run)[NT],
                                           float (&l_rnd)[NT], int lane, __bf16* gtile,
-                                          const int* grows, __amdgpu_buffer_rsrc_t kvr, int wave) {
+                                          const int* grows, bool gnext, int wave) {
     using C = FwdCfg<DQK, NW, NT>;
     using Tile = typename C::Tile;
     const int g = lane >> 4;
     static_assert(NW == 4, "the gather schedule assumes 16 main rows and 2 rope loads per wave");
-    const int gids = Tile::template row_ids<NW>(grows, wave, lane);
+    const int gids = Tile::template row_ids<NW>(grows, wave, lane, a.S_kv);
+    // the next block's gather reads nothing when there is no next block
+    const auto kvr = Tile::kv_rsrc_if(a.kv, a.S_kv, gnext);
 
     // The block's two halves in the order S(0), S(1), PV(0), PV(1): the
     // exponentials of half 0 run between the MFMAs of S(1) and those of half
@@ -208,7 +210,7 @@ __device__ __forceinline__ void fwd_block(const FwdArgs& a, const __bf16* tile,
     // the rope rows
     s_loop(H0{}, [&](int ks) {
         if (ks < 16) Tile::template gather_main_row<NW>(gtile, gids, kvr, wave, lane, ks);
-        else Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, ks - 16);
+        else Tile::template gather_rope_one<NW>(gtile, grows, kvr, wave, lane, ks - 16, a.S_kv);
     });
     prep(H0{});
     s_loop(H1{}, [&](int ks) {
@@ -306,6 +308,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         if (tid < BLK) {
             s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
             s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
+            s_rows[2][tid] = -1;     // written again before any block reads it
         }
         __syncthreads();
         if (pass == 0) {
@@ -314,15 +317,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
             nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1);
         }
-        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane);
+        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
 
         // Two blocks per iteration so that each tile is a distinct LDS object.
         // Block k: wait for its tile; store the slot rows of block k + 1
         // (their raw indices were loaded at block k - 1 and the wait just
         // covered that load: storing them any earlier would wait for the whole
         // gather issued since); load the raw indices of block k + 2; compute,
-        // issuing the gather of block k + 1 from inside the math (after the
-        // last block it loads rows nobody reads, into a free tile).
+        // issuing the gather of block k + 1 from inside the math (the last
+        // block issues none).
         int ahead = 0;
         for (int b = 0; b < nblk; b += 2) {
             // ---- block b in tile 0
@@ -334,9 +337,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             if (active)
                 fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane,
-                                       s_tile1, s_rows[(b + 1) % 3], kvr, wave);
-            else
-                Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane);
+                                       s_tile1, s_rows[(b + 1) % 3], b + 1 < nblk, wave);
+            else if (b + 1 < nblk)
+                Tile::template gather_async<NW>(s_tile1, s_rows[(b + 1) % 3], kvr, wave, lane, a.S_kv);
             if (b + 1 >= nblk) break;
             // ---- block b+1 in tile 1
             wait_vmem();
@@ -347,9 +350,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             if (active)
                 fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd,
-                                       lane, s_tile0, s_rows[(b + 2) % 3], kvr, wave);
-            else
-                Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane);
+                                       lane, s_tile0, s_rows[(b + 2) % 3], b + 2 < nblk, wave);
+            else if (b + 2 < nblk)
+                Tile::template gather_async<NW>(s_tile0, s_rows[(b + 2) % 3], kvr, wave, lane, a.S_kv);
         }
 
         // did any head's scores rise more than REF_SLACK above its reference?
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             far |= rmax[nt] > m_ref[nt] + REF_SLACK;
         }
         if (pass == 0 && active && __builtin_amdgcn_ballot_w64(far) != 0 && lane == 0) s_rerun = 1;
-        wait_vmem();                    // the spare gather after the last block
+        wait_vmem();
         __syncthreads();                // tiles and s_rows are free; s_rerun is final
         if (pass == 1 || s_rerun == 0) break;
 #pragma unroll

@@ -112,24 +112,39 @@ struct KvTileSwz {
     }
 
     // ---- gather.  Buffer loads straight into LDS: the KV rows are addressed
-    // through a buffer resource over kv (reads past S_kv rows would return 0;
-    // the row indices are clamped into range anyway), the KV row offset of a
-    // main row is a scalar, the lane's chunk offset a vector register.
+    // through a buffer resource over kv, the KV row offset of a main row is a
+    // scalar, the lane's chunk offset a vector register.  Row indices are
+    // clamped into [0, S_kv) before use (load_row).
     __device__ static __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* kv, int S_kv) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kv), (short)0, S_kv * DQK * 2,
                                                  0x00020000);
+    }
+
+    // The same resource with live == false: zero records, so every load
+    // through it is out of range (the range check covers the lane offset,
+    // and any offset is >= 0 records) and reads no memory.  Used for the
+    // gather after a row's last block, which would fill a free tile that
+    // nobody reads: selecting the resource keeps the issuing loops free of
+    // branches.
+    __device__ static __amdgpu_buffer_rsrc_t kv_rsrc_if(const __bf16* kv, int S_kv, bool live) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kv), (short)0,
+                                                 live ? S_kv * DQK * 2 : 0, 0x00020000);
     }
 
     // NW waves split the 64 main rows: wave w owns rows w * RPW .. + RPW - 1.
     template <int NW>
     static constexpr int RPW = BLK / NW;
 
+    // A slot row as a KV row to load: -1 (invalid slot) and anything outside
+    // [0, S_kv) load row 0.  The main-row offset is a scalar offset, which the
+    // buffer's range check does not cover, so every row stays in range here.
+    __device__ static int load_row(int r, int S_kv) { return (unsigned)r < (unsigned)S_kv ? r : 0; }
+
     // Lane l of wave w holds the KV row of tile row w * RPW + l % RPW (invalid
     // slots -> row 0); lane i's value is read back as a scalar per row.
     template <int NW>
-    __device__ static int row_ids(const int* s_row, int wave_s, int lane) {
-        const int r = s_row[wave_s * RPW<NW> + (lane & (RPW<NW> - 1))];
-        return r < 0 ? 0 : r;
+    __device__ static int row_ids(const int* s_row, int wave_s, int lane, int S_kv) {
+        return load_row(s_row[wave_s * RPW<NW> + (lane & (RPW<NW> - 1))], S_kv);
     }
 
     // Issue main row i (a compile-time constant, 0 <= i < RPW) of this wave.
@@ -147,13 +162,12 @@ struct KvTileSwz {
     // rope region, j = k NW + wave, one 16-byte chunk per lane.
     template <int NW>
     __device__ static void gather_rope_one(__bf16* tile, const int* s_row, __amdgpu_buffer_rsrc_t rs,
-                                           int wave_s, int lane, int k) {
+                                           int wave_s, int lane, int k, int S_kv) {
         if constexpr (ROPE) {
             static_assert(NW <= 8 && 8 % NW == 0, "rope loads must split evenly");
             const int j = k * NW + wave_s;
             const int row = 8 * j + (lane >> 3);
-            int r = s_row[row];
-            r = r < 0 ? 0 : r;
+            const int r = load_row(s_row[row], S_kv);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rs, (lds_void*)(reinterpret_cast<char*>(tile) + ROPE_OFF + 8 * j * ROPE_ROWB), 16,
                 r * (DQK * 2) + 1024 + (((lane & 7) ^ fr(row)) << 4), 0, 0, 0);
@@ -164,20 +178,20 @@ struct KvTileSwz {
     // over the waves).
     template <int NW>
     __device__ static void gather_rope(__bf16* tile, const int* s_row, __amdgpu_buffer_rsrc_t rs,
-                                       int wave_s, int lane) {
+                                       int wave_s, int lane, int S_kv) {
 #pragma unroll
-        for (int k = 0; k < 8 / NW; ++k) gather_rope_one<NW>(tile, s_row, rs, wave_s, lane, k);
+        for (int k = 0; k < 8 / NW; ++k) gather_rope_one<NW>(tile, s_row, rs, wave_s, lane, k, S_kv);
     }
 
     // The whole gather of one tile by this wave (the NW waves together fill
     // it).  No wait here.
     template <int NW>
     __device__ static void gather_async(__bf16* tile, const int* s_row, __amdgpu_buffer_rsrc_t rs,
-                                        int wave_s, int lane) {
-        const int ids = row_ids<NW>(s_row, wave_s, lane);
+                                        int wave_s, int lane, int S_kv) {
+        const int ids = row_ids<NW>(s_row, wave_s, lane, S_kv);
 #pragma unroll
         for (int i = 0; i < RPW<NW>; ++i) gather_main_row<NW>(tile, ids, rs, wave_s, lane, i);
-        gather_rope<NW>(tile, s_row, rs, wave_s, lane);
+        gather_rope<NW>(tile, s_row, rs, wave_s, lane, S_kv);
     }
 };
 
