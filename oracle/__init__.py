@@ -8,7 +8,8 @@ Modules
 -------
 ``smla``   per-token, per-slot definition of the forward and backward
            (``oracle_fwd``, ``oracle_bwd``) and of the exact Delta
-           (``oracle_delta_exact``), written out in fp64 NumPy.
+           (``oracle_delta_exact``) and of the sink gradient alone (``oracle_dsink``),
+           written out in fp64 NumPy.
 ``dense``  a second, independent formulation: dense masked attention over all
            KV rows in torch fp64, with autograd gradients.  It pins ``smla``.
 ``fd``     central finite differences of L = sum(dO * O), a third pin that
@@ -27,5 +28,5 @@ from .smla import (  # noqa: F401
     oracle_fwd,
     oracle_bwd,
     oracle_delta_exact,
-    fwd_flops,
+    oracle_dsink,
 )

@@ -44,7 +44,7 @@ __all__ = [
     "oracle_fwd",
     "oracle_bwd",
     "oracle_delta_exact",
-    "fwd_flops",
+    "oracle_dsink",
 ]
 
 
@@ -306,8 +306,39 @@ def oracle_delta_exact(q, kv, dO, topk_idxs, topk_length, attn_sink, scale, d_v,
     return delta
 
 
-def fwd_flops(H: int, d_qk: int, d_v: int, n_valid_slots: int) -> float:
-    """Forward FLOP convention of [flash-attn #2882] Performance: 2*H*K*(d_qk+d_v)
-    per token with K the valid gathered slots; the backward counts 2.5x."""
-    return 2.0 * H * n_valid_slots * (d_qk + d_v)
+def oracle_dsink(q, kv, dO, topk_idxs, topk_length, attn_sink, scale, d_v, delta_from="fp64",
+                 tokens=None):
+    """d_sink[h] = -sum_t p_sink[t,h] * Delta[t,h] on its own.
 
+    The sink gradient of oracle_bwd (the same passages: [cuDNN-FE #785]
+    Testing for the limit -sum(dP_sum) at p_sink = 1, Not addressed for
+    Delta), without the dQ and dKV products, so that it can run over every
+    token of a large problem: per token the probabilities, O = P V, Delta =
+    dO . O (O rounded to bf16 first for ``delta_from="bf16"``) and the
+    token's term.  Empty rows add nothing.  Returns d_sink [H] (None without
+    a sink).
+    """
+    if delta_from not in ("fp64", "bf16"):
+        raise ValueError(delta_from)
+    if attn_sink is None:
+        return None
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    T, H, d_qk = q.shape
+    S_kv = kv.shape[0]
+    sink = np.asarray(attn_sink, dtype=np.float64)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    d_sink = np.zeros(H)
+    for t in toks:
+        ln = None if topk_length is None else topk_length[t]
+        _, rows = valid_slots(topk_idxs[t], ln, S_kv)
+        if rows.size == 0:
+            continue
+        _, lse_cols, _, p = _token_probs(q[t], kv, rows, scale, sink, d_qk)
+        o_t = p @ kv[rows, :d_v]
+        if delta_from == "bf16":
+            o_t = round_to_bf16(o_t)
+        dl = (dO[t] * o_t).sum(axis=1)
+        d_sink -= p_sink(lse_cols, sink) * dl
+    return d_sink

@@ -647,6 +647,39 @@ def test_pages_sink_threshold_and_limits():
 
 
 # ---------------------------------------------------------------------------
+# the sink gradient alone (oracle_dsink)
+# ---------------------------------------------------------------------------
+def run_dsink(p, **kw):
+    return oracle.oracle_dsink(p["q"], p["kv"], p["dO"], p["topk_idxs"], p["topk_length"],
+                               p["attn_sink"], p["scale"], p["d_v"], **kw)
+
+
+@pytest.mark.parametrize("case", [c for c in range(len(CASES)) if CASES[c]["sink"] is not None])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_dsink_alone_equals_dense_autograd(case, seed):
+    """oracle_dsink against the sink gradient of the dense formulation
+    (torch fp64 autograd through a softmax with the sink as an extra column)."""
+    p = small_problem(seed, **CASES[case])
+    _, _, mask, sink = dense_of(p)
+    _, _, dsd = dense_loss_grads(torch.from_numpy(p["q"]), torch.from_numpy(p["kv"]),
+                                 torch.from_numpy(p["dO"]), mask, sink, p["scale"], p["d_v"])
+    np.testing.assert_allclose(run_dsink(p), dsd.numpy(), rtol=0, atol=1e-10)
+
+
+def test_dsink_alone_modes_and_limits():
+    """No sink gives None; a +inf sink with its own O gives 0 (Delta = 0);
+    the bf16-O mode moves d_sink only by the rounding of O; a token subset
+    sums that subset's terms."""
+    p = small_problem(12, T=9)
+    assert run_dsink(dict(p, attn_sink=None)) is None
+    assert np.all(run_dsink(dict(p, attn_sink=np.full(3, np.inf))) == 0.0)
+    a, b = run_dsink(p), run_dsink(p, delta_from="bf16")
+    assert np.abs(a - b).max() < 1e-2 * max(np.abs(a).max(), 1e-30) and not np.array_equal(a, b)
+    part = run_dsink(p, tokens=np.arange(0, 4)) + run_dsink(p, tokens=np.arange(4, 9))
+    np.testing.assert_allclose(part, a, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: each must fail at least one pin
 # ---------------------------------------------------------------------------
 def _all_pins_pass(seed=30):
