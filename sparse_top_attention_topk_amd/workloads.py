@@ -27,9 +27,21 @@ import numpy as np
 import torch
 
 __all__ = ["Problem", "make_problem", "make_batched", "make_degenerate", "make_block_gaps",
-           "pack_live_blocks", "segment", "PROBLEMS", "EDGE_HEADS", "DEGENERATE_KINDS"]
+           "pack_live_blocks", "segment", "make_spiky", "head_slice", "PROBLEMS", "EDGE_HEADS",
+           "EXTRA_HEADS", "DEGENERATE_KINDS"]
 
 EDGE_HEADS = (1, 24, 64, 96, 128)
+# head counts that leave the last group of 32 heads partly filled (the pages'
+# in-kernel padding validation set includes 72, 100 and 120)
+EXTRA_HEADS = (72, 80, 90, 100, 120)
+
+
+def _edge_seed(base, H):
+    """Seed of an edge-suite problem: base + position of H in EDGE_HEADS, or
+    base + 5 + position in EXTRA_HEADS."""
+    if H in EDGE_HEADS:
+        return base + EDGE_HEADS.index(H)
+    return base + len(EDGE_HEADS) + EXTRA_HEADS.index(H)
 
 
 @dataclass
@@ -133,7 +145,7 @@ def make_edge_compact(H, seed=None):
     rows forced to 0; slots < length hold distinct indices from [0,128); the
     tail holds random in-range indices that must be ignored by position."""
     if seed is None:
-        seed = 10 + EDGE_HEADS.index(H)
+        seed = _edge_seed(10, H)
     rng = np.random.default_rng(seed)
     T, S, dqk, dv, W = 128, 128, 576, 512, 64
     q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
@@ -156,7 +168,7 @@ def make_edge_wide(H, seed=None, T=128, S=256, W=1024):
     U{0..256} distinct indices at random slot positions, -1 elsewhere; one row
     with 0 valid and one with 256.  No sink."""
     if seed is None:
-        seed = 20 + EDGE_HEADS.index(H)
+        seed = _edge_seed(20, H)
     rng = np.random.default_rng(seed)
     dqk, dv = 576, 512
     q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, False)
@@ -284,7 +296,7 @@ def make_edge_sink(H, seed=None, sink_cycle_offset=0):
     chosen so that the largest score is -100 (rows whose projections are not
     all positive are redrawn)."""
     if seed is None:
-        seed = 30 + EDGE_HEADS.index(H)
+        seed = _edge_seed(30, H)
     rng = np.random.default_rng(seed)
     T, S, dqk, dv, W = 128, 128, 576, 512, 64
     scale = 1.0 / math.sqrt(dqk)
@@ -389,6 +401,91 @@ def segment(p: Problem, i: int) -> Problem:
                    p.attn_sink, meta=dict(parent=p.name, segment=i))
 
 
+def make_spiky(H, d_qk=576, seed=100, T=256, window=64, topk=128, frac=0.25, d_v=512,
+               spike=(80.0, 120.0)):
+    """DeepSeek-V4-like rows (window, then causal top-k; [window | top-k]
+    order) where some tokens hold one KV row whose score rises far above
+    everything in the token's first 64-slot block.
+
+    For a fraction ``frac`` of the tokens that have top-k slots past the
+    first block, one top-k slot j >= 64 is picked and its row r = idx[t, j];
+    for every other head h of that token q[t, h] is replaced by
+    g_h * kv[r] / |kv[r]| + 0.25 N(0, 1) with g_h drawn so that the score
+    scale * <q[t, h], kv[r]> lands near a value drawn from ``spike`` (in
+    nats), i.e. 60-100 nats above the N(0, 1)-scale scores of the first
+    block.  A further set of tokens (the same count) gets the spike in the
+    first block instead (window slot 0), which makes every later score tiny
+    next to it.  meta["late_spike"] / meta["early_spike"] list the tokens."""
+    rng = np.random.default_rng(seed)
+    q32 = rng.standard_normal(size=(T, H, d_qk), dtype=np.float32)
+    kv = _bf16(rng, (T, d_qk))
+    dO = _bf16(rng, (T, H, d_v))
+    sink = torch.from_numpy(rng.standard_normal(size=(H,), dtype=np.float32))
+    idx = _window_topk_idxs(rng, T, window, topk)
+    scale = 1.0 / math.sqrt(d_qk)
+    kvf = kv.double().numpy()
+    cand = np.nonzero((idx[:, 64:] >= 0).any(axis=1))[0]
+    n = max(1, int(round(frac * cand.size)))
+    picked = rng.choice(cand, size=min(2 * n, cand.size), replace=False)
+    late, early = sorted(int(t) for t in picked[:n]), sorted(int(t) for t in picked[n:])
+    for t in late + early:
+        if t in late:
+            slots = np.nonzero(idx[t, 64:] >= 0)[0] + 64
+            j = int(rng.choice(slots))
+        else:
+            j = 0
+        r = int(idx[t, j])
+        u = kvf[r] / np.linalg.norm(kvf[r])
+        for h in range(0, H, 2):
+            target = rng.uniform(*spike)
+            g = target / (scale * np.linalg.norm(kvf[r]))
+            q32[t, h] = (g * u + 0.25 * rng.standard_normal(d_qk)).astype(np.float32)
+    q = torch.from_numpy(q32).to(torch.bfloat16)
+    return Problem(f"spiky_h{H}_d{d_qk}", T, T, H, d_qk, d_v, window + topk, scale, q, kv, dO,
+                   torch.from_numpy(idx), None, sink,
+                   meta=dict(seed=seed, window=window, topk=topk, late_spike=late, early_spike=early))
+
+
+def head_slice(p: Problem, H: int) -> Problem:
+    """The first H heads of a problem (q, dO and the sink sliced)."""
+    return Problem(f"{p.name}_heads{H}", p.T, p.S_kv, H, p.d_qk, p.d_v, p.W, p.scale,
+                   p.q[:, :H].clone(), p.kv, p.dO[:, :H].clone(), p.topk_idxs, p.topk_length,
+                   None if p.attn_sink is None else p.attn_sink[:H].clone(),
+                   meta=dict(p.meta, head_slice=H))
+
+
+def with_zero_dO_past(p: Problem, H: int) -> Problem:
+    """The same problem with dO = 0 for every head h >= H."""
+    dO = p.dO.clone()
+    dO[:, H:] = 0
+    return Problem(p.name + f"_dO0from{H}", p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale, p.q, p.kv,
+                   dO, p.topk_idxs, p.topk_length, p.attn_sink, meta=dict(p.meta, dO_zero_from=H))
+
+
+def make_spiky_dsv4(T=4096, H=128, d_qk=576, topk=512, seed=2, frac=0.10, name=None):
+    """The DeepSeek-V4-like problem of the same seed (make_dsv4) where a
+    fraction ``frac`` of the tokens that have top-k slots past the first
+    block get a late score spike as in make_spiky (every other head's query
+    aligned with one of the token's top-k rows, 80-120 nats)."""
+    p = make_dsv4(T, H, d_qk, 512, topk, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    idx = p.topk_idxs.numpy()
+    q32 = p.q.float().numpy().copy()
+    kvf = p.kv.double().numpy()
+    cand = np.nonzero((idx[:, 64:] >= 0).any(axis=1))[0]
+    late = sorted(int(t) for t in rng.choice(cand, size=int(round(frac * cand.size)), replace=False))
+    for t in late:
+        slots = np.nonzero(idx[t, 64:] >= 0)[0] + 64
+        r = int(idx[t, int(rng.choice(slots))])
+        u = kvf[r] / np.linalg.norm(kvf[r])
+        g = rng.uniform(80.0, 120.0, size=(H + 1) // 2) / (p.scale * np.linalg.norm(kvf[r]))
+        q32[t, 0::2] = (g[:, None] * u[None, :] +
+                        0.25 * rng.standard_normal((g.size, d_qk))).astype(np.float32)
+    q = torch.from_numpy(q32).to(torch.bfloat16)
+    return Problem(name or f"{p.name}_spiky", p.T, p.S_kv, H, d_qk, 512, p.W, p.scale, q, p.kv, p.dO,
+                   p.topk_idxs, None, p.attn_sink, meta=dict(p.meta, late_spike=late))
+
+
 def make_problem(name: str, **kw) -> Problem:
     return PROBLEMS[name](**kw)
 
@@ -417,6 +514,13 @@ PROBLEMS = {
     **{f"grid_pro_h128_T{T}": (lambda T: lambda **kw: make_dsv4(T, 128, 512, 512, 1024, seed=60 + T // 4096,
                                                                  name=f"grid_pro_h128_T{T}", **kw))(T)
        for T in (4096, 8192, 16384)},
+    # the pages' T = 2048 comparison (flash H = 64 / H = 128, top-k 512, D = 512)
+    "grid_flash_h64_T2048": lambda **kw: make_dsv4(2048, 64, 512, 512, 512, seed=45,
+                                                   name="grid_flash_h64_T2048", **kw),
+    "grid_flash_h128_T2048": lambda **kw: make_dsv4(2048, 128, 512, 512, 512, seed=55,
+                                                    name="grid_flash_h128_T2048", **kw),
+    # the headline with 10 % of its tokens holding a late score spike
+    "dsv4_flash_h128_spiky": lambda **kw: make_spiky_dsv4(name="dsv4_flash_h128_T4096_spiky", **kw),
     # the headline's index sets packed to the front with topk_length
     "dsv4_flash_h128_compact": lambda **kw: make_dsv4(4096, 128, 576, 512, 512, seed=2, compact=True,
                                                       name="dsv4_flash_h128_T4096_compact", **kw),
