@@ -13,6 +13,19 @@ FLOP convention of the pages ([flash-attn #2882] Performance): forward
 2.5x the forward.  Gathered bytes (the pages' TB/s model): gathered KV rows
 (K * d_qk * 2 bytes per token) + Q read + O write.
 
+Roofline (``roofline`` for the longest stage, ``detail.stage_roofline`` for
+all): the method's own work per launch in the units of the hot-path table
+(FLOP of the products a stage computes; bytes of the method's inputs and
+outputs it touches, gathered KV rows counted per valid slot) against the
+MI355X peaks, with the binding roof the one whose ideal time is longer.  The
+library's intermediate buffers are not the method's bytes; the measured HBM
+traffic of the stage (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated,
+from profiles/) is reported next to them with its ratio, and the MFMA busy
+share from the counter profile.
+
+``detail.configs``: the other DeepSeek-V4-like workloads (H = 64, d = 512;
+T = 16384 pro) timed the same way with fewer steps (``--no-detail`` skips).
+
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: the library runs on
 one GPU.
 """
@@ -45,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2560,
                     help="tokens of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="skip timing the other DeepSeek-V4-like configurations")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
@@ -64,28 +79,13 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} requested; the library runs on one GPU only "
-              "(no collectives, no sharding).  Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    from sparse_top_attention_topk_amd import _lib, workloads as wl
+def run_workload(p, steps, warmup, n_event_steps=5, exact_delta=True):
+    """Time ``steps`` plain steps of problem p (inputs resident in HBM) and a
+    few more with HIP events at the stage boundaries.  Returns a dict of
+    times in ms."""
+    from sparse_top_attention_topk_amd import _lib
 
     dev = torch.device("cuda:0")
-    p = wl.make_problem(args.workload)
-    n_valid = p.valid_count()
-    fwd_flop = 2.0 * p.H * (p.d_qk + p.d_v) * n_valid
-    bwd_flop = 2.5 * fwd_flop
-    # the pages' timing tables count K = slots per token (W for every token),
-    # valid or not: a second figure in that convention, for comparison only
-    fwd_flop_nominal = 2.0 * p.H * (p.d_qk + p.d_v) * p.T * p.W
-    gathered = n_valid * p.d_qk * 2 + p.T * p.H * (p.d_qk + p.d_v) * 2
-
     q, kv, dO = p.q.to(dev), p.kv.to(dev), p.dO.to(dev)
     idx = p.topk_idxs.to(dev)
     length = None if p.topk_length is None else p.topk_length.to(dev)
@@ -120,47 +120,107 @@ def main():
                       d_sink=d_sink, workspace=ws, stream=stream,
                       stage_events=None if ev is None else ev[2:])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # the timed steps: plain calls (no events between the kernels)
     t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # per-stage times: the same steps again with events at the stage boundaries
-    evs = [new_events() for _ in range(min(args.steps, 5))]
+    evs = [new_events() for _ in range(max(1, min(steps, n_event_steps)))]
     torch.cuda.synchronize()
     for ev in evs:
         step(ev)
     torch.cuda.synchronize()
 
-    # the high-accuracy Delta (smla_bwd_delta_exact, in place of the
-    # preprocess): timed on its own after the steps, not part of `value`
-    delta_x = torch.empty_like(delta)
-    _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x, stream=stream)
-    ex0, ex1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ex0.record(stream)
-    for _ in range(3):
-        _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x, stream=stream)
-    ex1.record(stream)
-    torch.cuda.synchronize()
-    delta_exact_ms = ex0.elapsed_time(ex1) / 3
-
+    out = {"ms_per_step": wall * 1e3 / steps, "ws_bytes": ws_bytes}
     names = ["fwd", "preprocess"] + list(_lib.BWD_STAGES)
-    stage_ms = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                for i, nm in enumerate(names)}
-    step_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
-    ms_per_step = wall * 1e3 / args.steps
+    out["stage_ms"] = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                       for i, nm in enumerate(names)}
+    out["step_ms_events"] = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
+
+    if exact_delta:
+        # the high-accuracy Delta (smla_bwd_delta_exact, in place of the
+        # preprocess): timed on its own after the steps, not part of `value`
+        delta_x = torch.empty_like(delta)
+        _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x, stream=stream)
+        ex0, ex1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ex0.record(stream)
+        for _ in range(3):
+            _lib.smla_bwd_delta_exact(q, kv, dO, lse, idx, length, sink, p.scale, delta=delta_x,
+                                      stream=stream)
+        ex1.record(stream)
+        torch.cuda.synchronize()
+        out["delta_exact_ms"] = ex0.elapsed_time(ex1) / 3
+    del q, kv, dO, idx, o, lse, delta, dq, dkv, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def flops_and_bytes(p):
+    n_valid = p.valid_count()
+    fwd_flop = 2.0 * p.H * (p.d_qk + p.d_v) * n_valid
+    # the pages' timing tables count K = slots per token (W for every token),
+    # valid or not: a second figure in that convention, for comparison only
+    fwd_flop_nominal = 2.0 * p.H * (p.d_qk + p.d_v) * p.T * p.W
+    gathered = n_valid * p.d_qk * 2 + p.T * p.H * (p.d_qk + p.d_v) * 2
+    return n_valid, fwd_flop, 2.5 * fwd_flop, fwd_flop_nominal, gathered
+
+
+def config_line(p, t):
+    """Times and rates of one workload (fwd, bwd incl. preprocess, step)."""
+    n_valid, fwd_flop, bwd_flop, nominal, gathered = flops_and_bytes(p)
+    fwd_ms = t["stage_ms"]["fwd"]
+    bwd_ms = t["step_ms_events"] - fwd_ms
+    return {
+        "T": p.T, "H": p.H, "d_qk": p.d_qk, "W": p.W, "valid_slots": n_valid,
+        "fwd_us": round(fwd_ms * 1e3, 1), "bwd_us": round(bwd_ms * 1e3, 1),
+        "step_us": round(t["ms_per_step"] * 1e3, 1),
+        "step_tflops": round((fwd_flop + bwd_flop) / (t["ms_per_step"] * 1e-3) / 1e12, 1),
+        "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 1),
+        "fwd_gathered_tbs": round(gathered / (fwd_ms * 1e-3) / 1e12, 3),
+        "workspace_gb": round(t["ws_bytes"] / 1e9, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested; the library runs on one GPU only "
+              "(no collectives, no sharding).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from sparse_top_attention_topk_amd import workloads as wl
+
+    p = wl.make_problem(args.workload)
+    n_valid, fwd_flop, bwd_flop, fwd_flop_nominal, gathered = flops_and_bytes(p)
+    t = run_workload(p, args.steps, args.warmup)
+    stage_ms, step_ms, ms_per_step = t["stage_ms"], t["step_ms_events"], t["ms_per_step"]
     total_flop = fwd_flop + bwd_flop
     value = total_flop / (ms_per_step * 1e-3) / 1e12
     work = stage_work(p, n_valid)
-    dominant = max(stage_ms, key=lambda k: stage_ms[k])
+    dominant = max((k for k in stage_ms if k in work), key=lambda k: stage_ms[k])
     roofline = roofline_for(dominant, stage_ms[dominant] * 1e-3, work[dominant], p.name)
     fwd_s = stage_ms["fwd"] * 1e-3
+
+    # the other DeepSeek-V4-like configurations, timed the same way (fewer steps)
+    configs = {}
+    if not args.no_detail:
+        for name in ("dsv4_flash_h64", "dsv4_pro"):
+            if name == args.workload:
+                continue
+            q = wl.make_problem(name)
+            configs[name] = config_line(q, run_workload(q, 3, 1, n_event_steps=2, exact_delta=False))
+            del q
 
     cpu = None
     if not args.no_cpu:
@@ -198,13 +258,17 @@ def main():
             "fwd_mfma_frac": round(fwd_flop / fwd_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "fwd_bwd_mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
             "fwd_flop": fwd_flop, "bwd_flop": bwd_flop, "gathered_bytes_fwd": gathered,
+            "workspace_gb": round(t["ws_bytes"] / 1e9, 3),
             "tflops_nominal_k": {
                 "fwd": round(fwd_flop_nominal / fwd_s / 1e12, 1),
                 "bwd": round(2.5 * fwd_flop_nominal / ((step_ms - stage_ms["fwd"]) * 1e-3) / 1e12, 1),
                 "step": round(3.5 * fwd_flop_nominal / (ms_per_step * 1e-3) / 1e12, 1),
             },
-            "delta_exact_us": round(delta_exact_ms * 1e3, 1),
-            "step_us_exact_delta_mode": round((step_ms - stage_ms["preprocess"] + delta_exact_ms) * 1e3, 1),
+            "stage_roofline": {k: roofline_for(k, stage_ms[k] * 1e-3, work[k], p.name, brief=True)
+                               for k in stage_ms if k in work},
+            "delta_exact_us": round(t["delta_exact_ms"] * 1e3, 1),
+            "step_us_exact_delta_mode": round((step_ms - stage_ms["preprocess"] + t["delta_exact_ms"]) * 1e3, 1),
+            "configs": configs,
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -221,18 +285,25 @@ STAGE_KERNEL = {"fwd": ("fwd_kernel",), "preprocess": ("preprocess_kernel",),
 
 
 def stage_work(p, n):
-    """Algorithmic work per launch of each stage: (FLOP, bytes).  n = valid
-    (token, slot) pairs.  Gathered KV rows count 2 * d_qk bytes per valid slot
-    (the pages' model); partials are 2 bytes per value per valid slot."""
+    """The method's algorithmic work per launch of each stage, in the units of
+    the hot-path table: (FLOP, bytes).  n = valid (token, slot) pairs.  A
+    valid slot is 2 H (d_qk + d_v) FLOP of S and PV (forward), of S and dP
+    (recompute) and of dK and dV, and 2 H d_qk of dQ; gathered KV rows count
+    2 d_qk bytes per valid slot (the pages' model).  Per token: q, O, dO, dQ
+    are 2 H d bytes each.  The library's own intermediate buffers (P and dS,
+    the per-slot dKV partials) are not the method's bytes: they show up in the
+    measured traffic, which is reported next to these."""
     T, H, dqk, dv, S, W = p.T, p.H, p.d_qk, p.d_v, p.S_kv, p.W
+    qb, ob = T * H * dqk * 2, T * H * dv * 2
+    gath = n * dqk * 2
     return {
-        "fwd": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2),
-        "preprocess": (0.0, 2 * T * H * dv * 2 + T * H * 4),
-        "index_inversion": (0.0, 2 * T * W * 4 + n * 4),
-        "sdp": (2.0 * H * (dqk + dv) * n, n * dqk * 2 + T * H * (dqk + dv) * 2 + 2 * H * n * 2),
-        "dq": (2.0 * H * dqk * n, n * dqk * 2 + H * n * 2 + T * H * dqk * 2),
-        "dkv": (2.0 * H * (dqk + dv) * n, 2 * H * n * 2 + T * H * (dqk + dv) * 2 + n * dqk * 2),
-        "dkv_reduce": (0.0, n * dqk * 2 + n * 4 + S * dqk * 4),
+        "fwd": (2.0 * H * (dqk + dv) * n, gath + qb + ob + T * W * 4 + T * H * 4),
+        "preprocess": (0.0, 2 * ob + T * H * 4),
+        "index_inversion": (0.0, T * W * 4),
+        "sdp": (2.0 * H * (dqk + dv) * n, gath + qb + ob),
+        "dq": (2.0 * H * dqk * n, gath + qb),
+        "dkv": (2.0 * H * (dqk + dv) * n, qb + ob),
+        "dkv_reduce": (0.0, S * dqk * 4),
         "dsink": (0.0, 2 * T * H * 4),
     }
 
@@ -246,25 +317,51 @@ def source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(stage, workload):
-    """HBM bytes per launch of the stage's kernel(s) from the committed counter
-    profile (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
-    kernel sources changed since it was taken or it covers another workload."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_dsv4_flash_h128.json")
+def _profile(fname, workload):
+    """A committed counter profile (JSON) if it was taken on this workload with
+    the current kernel sources, else None."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", fname)) as f:
             rec = json.load(f)
     except OSError:
         return None
     if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
         return None
+    return rec
+
+
+def _per_stage(rec, stage, key, combine=sum):
     frags = STAGE_KERNEL[stage]
-    vals = [k["bytes_per_launch"] for name, k in rec["kernels"].items()
-            if any(f in name for f in frags)]
-    return int(sum(vals)) if vals else None
+    vals = [k[key] for name, k in rec["kernels"].items() if any(f in name for f in frags) and key in k]
+    return combine(vals) if vals else None
 
 
-def roofline_for(stage, seconds, work, workload):
+def measured_traffic(stage, workload):
+    """HBM bytes per launch of the stage's kernel(s) from the committed counter
+    profile (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    kernel sources changed since it was taken or it covers another workload."""
+    rec = _profile("hbm_traffic_dsv4_flash_h128.json", workload)
+    if rec is None:
+        return None
+    v = _per_stage(rec, stage, "bytes_per_launch")
+    return None if v is None else int(v)
+
+
+def measured_mfma_util(stage, workload):
+    """MFMA busy share of the stage's main kernel from the committed counter
+    profile: sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x
+    1024 SIMDs), the rocprofv3 MfmaUtil definition; None if unavailable."""
+    rec = _profile("mfma_util_dsv4_flash_h128.json", workload)
+    if rec is None:
+        return None
+    return _per_stage(rec, stage, "mfma_util", combine=max)
+
+
+def roofline_for(stage, seconds, work, workload, brief=False):
+    """Roofline of one stage in the method's units: the binding roof is the
+    one with the longer ideal time (FLOP at the bf16 MFMA peak, or bytes at
+    the HBM peak); achieved = the method's work / the stage's event-timed
+    duration."""
     flop, nbytes = work
     t_mfma = flop / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
@@ -272,12 +369,18 @@ def roofline_for(stage, seconds, work, workload):
         achieved, peak, unit, bound = flop / seconds / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = nbytes / seconds / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
-    return {
-        "kernel": stage, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
-        "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(stage, workload),
-        "avg_launch_us": round(seconds * 1e6, 1), "algorithmic_flop": flop,
-        "algorithmic_bytes": int(nbytes),
-    }
+    traffic = measured_traffic(stage, workload)
+    out = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "avg_launch_us": round(seconds * 1e6, 1)}
+    if brief:
+        return out
+    out.update({
+        "kernel": stage, "traffic": traffic,
+        "traffic_over_algorithmic_bytes": None if traffic is None else round(traffic / nbytes, 3),
+        "mfma_util_counters": measured_mfma_util(stage, workload),
+        "algorithmic_flop": flop, "algorithmic_bytes": int(nbytes),
+    })
+    return out
 
 
 def cpu_baseline(p, n_tokens):
