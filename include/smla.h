@@ -29,9 +29,10 @@
  *     pointers.  bf16 tensors are passed as void* holding IEEE bfloat16.
  *   - B > 1 batches are expressed by concatenating tokens and KV rows with
  *     global row indices.
- *   - Supported: d_qk in {512, 576}, d_v = 512, 1 <= H <= 128, W >= 1,
- *     1 <= S_kv <= SMLA_MAX_S_KV, T >= 0 (T = 0 is a no-op), scale finite,
- *     T * (W rounded up to 64) < 2^31.
+ *   - Supported: d_qk in {512, 576}, d_v = 512, 1 <= H <= 128,
+ *     1 <= W <= SMLA_MAX_W, S_kv >= 1 with S_kv * d_qk * 2 < 2^31 (KV rows
+ *     are addressed with 32-bit byte offsets: S_kv <= 1864135 at d_qk = 576,
+ *     2097151 at 512), T >= 0 (T = 0 is a no-op), scale finite.
  *   - The caller owns every buffer.  The library never allocates or frees
  *     memory and never synchronises: work is enqueued on `stream` (a
  *     hipStream_t; NULL means the null stream) and the call returns.
@@ -50,16 +51,20 @@
 extern "C" {
 #endif
 
-/* Largest supported number of KV rows (one 4-byte counter per row in LDS). */
-#define SMLA_MAX_S_KV 40960
+/* Largest supported top-k width W (slots per token). */
+#define SMLA_MAX_W (1 << 24)
+
+/* Workspace that smla_bwd_workspace_size asks for at most, unless one token's
+ * chunk alone needs more (8 GiB). */
+#define SMLA_BWD_DEFAULT_WORKSPACE ((size_t)8 << 30)
 
 typedef enum {
     SMLA_OK = 0,
     SMLA_ERR_NULL = 1,        /* a required pointer is NULL                  */
     SMLA_ERR_SHAPE = 2,       /* a size is negative or inconsistent          */
-    SMLA_ERR_UNSUPPORTED = 3, /* d_qk / d_v / H outside the supported range  */
+    SMLA_ERR_UNSUPPORTED = 3, /* a size outside the supported range          */
     SMLA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned       */
-    SMLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required     */
+    SMLA_ERR_WORKSPACE = 5,   /* workspace NULL or too small for one token   */
     SMLA_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch     */
 } smla_status;
 
@@ -113,8 +118,12 @@ smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const voi
                                  const int32_t* topk_length, const float* attn_sink,
                                  float* delta, void* stream);
 
-/* Bytes of device workspace smla_bwd needs for these sizes (0 if T == 0).
- * Returns 0 for unsupported sizes as well; smla_bwd reports the error. */
+/* Bytes of device workspace to give smla_bwd for these sizes (0 if T == 0):
+ * the workspace of all T tokens at once when that is at most
+ * SMLA_BWD_DEFAULT_WORKSPACE, else that of equal token chunks that fit in it
+ * (never less than what one token needs).  Returns 0 for unsupported sizes
+ * as well; smla_bwd reports the error.  smla_bwd accepts any larger or
+ * smaller workspace down to one token's need and sizes its chunks to it. */
 size_t smla_bwd_workspace_size(const smla_dims* dims);
 
 /* Backward of L = sum(dO * O) [cuDNN-FE #785 Summary 1-3, Why 1-3;
@@ -135,8 +144,14 @@ size_t smla_bwd_workspace_size(const smla_dims* dims);
  *              p_sink = sigmoid(sink - lse); required iff attn_sink != NULL
  * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16
  * [T, H, d_v]; lse fp32 [T, H] from smla_fwd; delta fp32 [T, H] from
- * smla_bwd_preprocess or smla_bwd_delta_exact.  workspace: device memory of at least
- * smla_bwd_workspace_size(dims) bytes, used by this call only.
+ * smla_bwd_preprocess or smla_bwd_delta_exact.  workspace: workspace_bytes
+ * of device memory (16-byte aligned), used by this call only.  The tokens
+ * are processed in chunks of equal size, as many tokens per chunk as the
+ * workspace holds (all T with smla_bwd_workspace_size bytes unless that is
+ * capped); dkv sums a row's contributions chunk by chunk in token order, so
+ * its bits depend on the chunk size but not on scheduling.
+ * SMLA_ERR_WORKSPACE if workspace is NULL or holds less than one token's
+ * chunk.
  */
 smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const void* dO,
                      const float* lse, const float* delta, const int32_t* topk_idxs,
@@ -168,7 +183,9 @@ smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv
 /* smla_bwd with stage timing, for benchmarks and profilers.  Computes exactly
  * what smla_bwd computes (same passages, same kernels) and in addition records
  * stage_events[0] on `stream` before the first stage and stage_events[i] after
- * stage i (i = 1..SMLA_BWD_STAGES).  stage_events: n_events >= 
+ * stage i (i = 1..SMLA_BWD_STAGES).  When the workspace splits the tokens into
+ * several chunks, events 1..5 bracket the stages of the first chunk and the
+ * last event follows the whole call.  stage_events: n_events >= 
  * SMLA_BWD_STAGES + 1 hipEvent_t handles created by the caller (recorded, not
  * created or destroyed, by the library).  Errors: SMLA_ERR_NULL for a NULL
  * array or handle, SMLA_ERR_SHAPE if n_events is too small, then as smla_bwd.

@@ -13,10 +13,9 @@ smla_status check_dims(const smla_dims* d) {
     if (d->T < 0 || d->S_kv < 1 || d->H < 1 || d->W < 1) return SMLA_ERR_SHAPE;
     if ((d->d_qk != 512 && d->d_qk != 576) || d->d_v != 512 || d->H > 128)
         return SMLA_ERR_UNSUPPORTED;
-    // the backward's index inversion keeps one counter per KV row in LDS, and
-    // flat slot indices t * Wp + j must fit in int32
-    if (d->S_kv > SMLA_MAX_S_KV) return SMLA_ERR_UNSUPPORTED;
-    if ((int64_t)d->T * (((int64_t)d->W + 63) / 64 * 64) >= INT32_MAX) return SMLA_ERR_UNSUPPORTED;
+    // KV rows are addressed with 32-bit byte offsets; slot positions of a
+    // row with 32-bit offsets as well
+    if ((int64_t)d->S_kv * d->d_qk * 2 > INT32_MAX || d->W > SMLA_MAX_W) return SMLA_ERR_UNSUPPORTED;
     if (!(d->scale == d->scale) || d->scale == INFINITY || d->scale == -INFINITY)
         return SMLA_ERR_SHAPE;
     return SMLA_OK;
@@ -26,42 +25,75 @@ size_t round_up_blk(int W) { return ((size_t)W + smla::BLK - 1) / smla::BLK * sm
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// tokens per chunk of the backward's index inversion (at most 256 chunks)
-int token_chunk(int T) { return T > 256 ? (T + 255) / 256 : 1; }
+// Sub-chunks of a token chunk of C tokens in the index inversion: at most
+// 256, and at most 16M counters in all (nsub x S_kv), so the counters stay
+// within 64 MB for any number of KV rows.
+int inversion_subchunks(const smla_dims* d, int C) {
+    int64_t n = 256;
+    const int64_t cap = ((int64_t)1 << 24) / d->S_kv;
+    if (n > cap) n = cap > 0 ? cap : 1;
+    if (n > C) n = C;
+    return (int)n;
+}
 
-// Workspace layout of smla_bwd (each region 256-byte aligned):
-//   P, scale*dS      bf16 [T, H, Wp] each (Wp = W rounded up to 64)
-//   chunk_cnt        int32 [ceil(T / tchunk), S_kv], tchunk = ceil(T / 256)
+// Workspace layout of smla_bwd for token chunks of C tokens (each region
+// 256-byte aligned):
+//   P, scale*dS      bf16 [C, H, Wp] each (Wp = W rounded up to 64)
+//   chunk_cnt        int32 [nsub, S_kv]
 //   row_cnt          int32 [S_kv]; row_off int32 [S_kv + 1]
-//   entries          int32 [T * W]
-//   partial          [T * Wp] rows of d_qk values in 4-value blocks (2 * d_qk bytes)
+//   entries          int32 [C * W]
+//   partial          [C * Wp] rows of d_qk values in 4-value blocks (2 * d_qk bytes)
 //   part_off         int32 [S_kv + 1]; part_row int32 [max_parts]
-//   part_sum         fp32 [max_parts, d_qk], max_parts = T * W / 64 + S_kv
+//   part_sum         fp32 [max_parts, d_qk], max_parts = C * W / 64 + min(S_kv, C * W)
+//                    (a row named n times has ceil(n / 64) parts)
 struct WsLayout {
     size_t p, ds, chunk, cnt, off, ent, part, poff, prow, psum, total;
-    int max_parts;
+    int max_parts, nsub;
 };
 
-WsLayout ws_layout(const smla_dims* d) {
+WsLayout ws_layout(const smla_dims* d, int C) {
     WsLayout L;
     const size_t Wp = round_up_blk(d->W);
-    const size_t pd = (size_t)d->T * d->H * Wp * sizeof(uint16_t);
-    const size_t tch = token_chunk(d->T);
-    const size_t nch = ((size_t)d->T + tch - 1) / tch;
+    const size_t pd = (size_t)C * d->H * Wp * sizeof(uint16_t);
+    L.nsub = inversion_subchunks(d, C);
+    const size_t cw = (size_t)C * d->W;
     L.p = 0;
     L.ds = align256(L.p + pd);
     L.chunk = align256(L.ds + pd);
-    L.cnt = align256(L.chunk + nch * d->S_kv * sizeof(int32_t));
+    L.cnt = align256(L.chunk + (size_t)L.nsub * d->S_kv * sizeof(int32_t));
     L.off = align256(L.cnt + (size_t)d->S_kv * sizeof(int32_t));
     L.ent = align256(L.off + ((size_t)d->S_kv + 1) * sizeof(int32_t));
-    L.part = align256(L.ent + (size_t)d->T * d->W * sizeof(int32_t));
-    L.poff = align256(L.part + (size_t)d->T * Wp * d->d_qk * 2);
-    const size_t mp = (size_t)d->T * d->W / 64 + d->S_kv;
+    L.part = align256(L.ent + cw * sizeof(int32_t));
+    L.poff = align256(L.part + (size_t)C * Wp * d->d_qk * 2);
+    const size_t mp = cw / 64 + ((size_t)d->S_kv < cw ? (size_t)d->S_kv : cw);
     L.max_parts = (int)mp;
     L.prow = align256(L.poff + ((size_t)d->S_kv + 1) * sizeof(int32_t));
     L.psum = align256(L.prow + mp * sizeof(int32_t));
     L.total = align256(L.psum + mp * d->d_qk * sizeof(float));
     return L;
+}
+
+// Largest chunk whose workspace fits in `bytes` (0 if not even one token's
+// does).  Local slot indices (t - t0) * Wp + j and part counts stay in int32.
+int max_chunk(const smla_dims* d, size_t bytes) {
+    const int64_t Wp = (int64_t)round_up_blk(d->W);
+    int64_t hi = d->T;
+    const int64_t lim = (INT32_MAX / 2) / Wp;
+    if (hi > lim) hi = lim;
+    if (hi < 1 || ws_layout(d, 1).total > bytes) return 0;
+    int64_t lo = 1;                    // fits
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (ws_layout(d, (int)mid).total <= bytes) lo = mid;
+        else hi = mid - 1;
+    }
+    return (int)lo;
+}
+
+// The same number of chunks with their sizes balanced.
+int balanced_chunk(const smla_dims* d, int cmax) {
+    const int64_t n = ((int64_t)d->T + cmax - 1) / cmax;
+    return (int)(((int64_t)d->T + n - 1) / n);
 }
 
 }  // namespace
@@ -73,9 +105,11 @@ const char* smla_status_string(smla_status s) {
         case SMLA_OK: return "ok";
         case SMLA_ERR_NULL: return "a required pointer is NULL";
         case SMLA_ERR_SHAPE: return "a size is negative or inconsistent";
-        case SMLA_ERR_UNSUPPORTED: return "unsupported d_qk / d_v / H";
+        case SMLA_ERR_UNSUPPORTED:
+            return "unsupported sizes: d_qk must be 512 or 576, d_v 512, H at most 128, "
+                   "S_kv * d_qk * 2 below 2^31 and W at most 2^24";
         case SMLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
-        case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SMLA_ERR_WORKSPACE: return "workspace missing or smaller than one token's chunk needs";
         case SMLA_ERR_LAUNCH: return "kernel launch failed";
     }
     return "unknown status";
@@ -136,6 +170,8 @@ smla_status smla_bwd_delta_exact(const smla_dims* d, const void* q, const void* 
     a.sink = attn_sink;
     a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
     a.Wp = (int)round_up_blk(d->W);
+    a.t0 = 0;
+    a.Tc = d->T;
     a.scale = d->scale;
     a.scale_log2 = d->scale * smla::LOG2E;
     hipError_t e = smla::launch_delta_exact(d->d_qk, a, static_cast<hipStream_t>(stream));
@@ -144,7 +180,14 @@ smla_status smla_bwd_delta_exact(const smla_dims* d, const void* q, const void* 
 
 size_t smla_bwd_workspace_size(const smla_dims* d) {
     if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
-    return ws_layout(d).total;
+    // one chunk (every token at once) when that fits the default budget,
+    // else balanced chunks within it; never less than one token's workspace
+    const int whole = max_chunk(d, ws_layout(d, d->T).total);
+    if (whole == d->T && ws_layout(d, d->T).total <= SMLA_BWD_DEFAULT_WORKSPACE)
+        return ws_layout(d, d->T).total;
+    int c = max_chunk(d, SMLA_BWD_DEFAULT_WORKSPACE);
+    if (c == 0) c = 1;
+    return ws_layout(d, balanced_chunk(d, c)).total;
 }
 
 // o == NULL: delta is an input (from the preprocess or the exact pass).
@@ -163,9 +206,15 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
         if (!aligned16(q) || !aligned16(kv) || !aligned16(dO) || !aligned16(dq) || !aligned16(dkv))
             return SMLA_ERR_ALIGN;
         if (o != nullptr && !aligned16(o)) return SMLA_ERR_ALIGN;
-        const size_t need = smla_bwd_workspace_size(d);
-        if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+        if (workspace == nullptr) return SMLA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return SMLA_ERR_ALIGN;
+    }
+    // tokens per chunk: as many as the workspace given holds (balanced)
+    int C = 1;
+    if (d->T > 0) {
+        C = max_chunk(d, workspace_bytes);
+        if (C == 0) return SMLA_ERR_WORKSPACE;
+        C = balanced_chunk(d, C);
     }
     smla::BwdArgs a = {};
     a.q = static_cast<const __bf16*>(q);
@@ -182,8 +231,11 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
     a.dkv = dkv;
     a.T = d->T; a.S_kv = d->S_kv; a.H = d->H; a.W = d->W;
     a.Wp = (int)round_up_blk(d->W);
-    a.tchunk = token_chunk(d->T);
-    const WsLayout WL = ws_layout(d);
+    a.t0 = 0;
+    a.Tc = C;
+    const WsLayout WL = ws_layout(d, C);
+    a.nsub = WL.nsub;
+    a.tchunk = (C + WL.nsub - 1) / WL.nsub;
     char* ws = static_cast<char*>(workspace);
     a.ws_p = reinterpret_cast<__bf16*>(ws + WL.p);
     a.ws_ds = reinterpret_cast<__bf16*>(ws + WL.ds);

@@ -73,14 +73,16 @@ hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, in
 }
 
 // ---------------------------------------------------------------------------
-// Index inversion: the valid (token, slot) pairs grouped by KV row.
-// Tokens are cut into at most 256 chunks of tchunk consecutive tokens.  rows_count counts,
-// per chunk, the valid slots naming each row (LDS counters); rows_scan turns
-// the counts into row segments and per-chunk offsets inside them; rows_fill
-// walks each chunk's tokens in order and appends every valid slot's flat index
-// t * Wp + j to its row.  A row's list is therefore in token order, so the
-// reduce sums each row in a fixed order: dKV does not depend on scheduling.
-// (Two slots of one token naming the same row carry identical
+// Index inversion of one token chunk: its valid (token, slot) pairs grouped
+// by KV row.  The chunk's tokens are cut into nsub sub-chunks of tchunk
+// consecutive tokens.  rows_count counts, per sub-chunk, the valid slots
+// naming each row (LDS counters, one workgroup per sub-chunk and range of
+// INV_ROWS rows); rows_chunkscan and rows_scan turn the counts into row
+// segments and per-sub-chunk offsets inside them; rows_fill walks each
+// sub-chunk's tokens in order and appends every valid slot's local flat index
+// (t - t0) * Wp + j to its row.  A row's list is therefore in token order,
+// so the reduce sums each row in a fixed order: dKV does not depend on
+// scheduling.  (Two slots of one token naming the same row carry identical
 // contributions, so their relative order cannot change a sum.)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fill_i32_kernel(int* __restrict__ p, int v, size_t n) {
@@ -88,21 +90,34 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int* __restrict__ p, int 
         p[i] = v;
 }
 
+// tokens [t_begin, t_end) of sub-chunk c and rows [r0, r0 + nr) of range blockIdx.y
+struct InvPart {
+    int t_begin, t_end, r0, nr;
+    __device__ InvPart(const BwdArgs& a) {
+        const int c = blockIdx.x;
+        const int chunk_end = a.t0 + a.Tc;
+        t_begin = a.t0 + c * a.tchunk;
+        t_end = t_begin + a.tchunk < chunk_end ? t_begin + a.tchunk : chunk_end;
+        r0 = (int)blockIdx.y * INV_ROWS;
+        nr = a.S_kv - r0 < INV_ROWS ? a.S_kv - r0 : INV_ROWS;
+    }
+};
+
 __global__ __launch_bounds__(256) void rows_count_kernel(BwdArgs a) {
-    extern __shared__ int s_cnt[];           // [S_kv]
-    const int c = blockIdx.x;
-    for (int r = threadIdx.x; r < a.S_kv; r += 256) s_cnt[r] = 0;
+    extern __shared__ int s_cnt[];           // [nr]
+    const InvPart P(a);
+    for (int i = threadIdx.x; i < P.nr; i += 256) s_cnt[i] = 0;
     __syncthreads();
-    const int t1 = (c + 1) * a.tchunk < a.T ? (c + 1) * a.tchunk : a.T;
-    for (int t = c * a.tchunk; t < t1; ++t) {
+    for (int t = P.t_begin; t < P.t_end; ++t) {
         const int L = row_length(a.len, t, a.W);
         for (int j = threadIdx.x; j < L; j += 256) {
-            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j);
-            if (r >= 0) atomicAdd(s_cnt + r, 1);
+            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j) - P.r0;
+            if ((unsigned)r < (unsigned)P.nr) atomicAdd(s_cnt + r, 1);
         }
     }
     __syncthreads();
-    for (int r = threadIdx.x; r < a.S_kv; r += 256) a.chunk_cnt[(size_t)c * a.S_kv + r] = s_cnt[r];
+    for (int i = threadIdx.x; i < P.nr; i += 256)
+        a.chunk_cnt[(size_t)blockIdx.x * a.S_kv + P.r0 + i] = s_cnt[i];
 }
 
 // Per row: running offsets over the chunks (chunk_cnt becomes the exclusive
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(256) void rows_chunkscan_kernel(BwdArgs a) {
     __shared__ int s_sum[8][32];
     const int rl = threadIdx.x & 31, part = threadIdx.x >> 5;
     const int r = (int)blockIdx.x * 32 + rl;
-    const int nch = (a.T + a.tchunk - 1) / a.tchunk;
+    const int nch = a.nsub;
     const int per = (nch + 7) / 8;
     const int c0 = part * per < nch ? part * per : nch;
     const int c1 = c0 + per < nch ? c0 + per : nch;
@@ -186,19 +201,18 @@ __global__ __launch_bounds__(256) void rows_parts_kernel(BwdArgs a) {
 }
 
 __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
-    extern __shared__ int s_cur[];           // [S_kv]
-    const int c = blockIdx.x;
-    for (int r = threadIdx.x; r < a.S_kv; r += 256)
-        s_cur[r] = a.row_off[r] + a.chunk_cnt[(size_t)c * a.S_kv + r];
+    extern __shared__ int s_cur[];           // [nr]
+    const InvPart P(a);
+    for (int i = threadIdx.x; i < P.nr; i += 256)
+        s_cur[i] = a.row_off[P.r0 + i] + a.chunk_cnt[(size_t)blockIdx.x * a.S_kv + P.r0 + i];
     __syncthreads();
-    const int t1 = (c + 1) * a.tchunk < a.T ? (c + 1) * a.tchunk : a.T;
-    for (int t = c * a.tchunk; t < t1; ++t) {
+    for (int t = P.t_begin; t < P.t_end; ++t) {
         const int L = row_length(a.len, t, a.W);
         for (int j = threadIdx.x; j < L; j += 256) {
-            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j);
-            if (r >= 0) a.entries[atomicAdd(s_cur + r, 1)] = t * a.Wp + j;
+            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j) - P.r0;
+            if ((unsigned)r < (unsigned)P.nr) a.entries[atomicAdd(s_cur + r, 1)] = (t - a.t0) * a.Wp + j;
         }
-        __syncthreads();                     // token order within the chunk
+        __syncthreads();                     // token order within the sub-chunk
     }
 }
 
@@ -411,7 +425,7 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
                 }
             }
             if (head < a.H) {
-                const size_t base = ((size_t)t * a.H + head) * a.Wp + b * BLK + half * 32 + 4 * g;
+                const size_t base = ((size_t)(t - a.t0) * a.H + head) * a.Wp + b * BLK + half * 32 + 4 * g;
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     st4(a.ws_p + base + m * 16, cvt4(pv[m][0], pv[m][1], pv[m][2], pv[m][3]));
@@ -467,7 +481,7 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int t = a.T - 1 - (int)blockIdx.x;
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
     const int h_wave = (int)blockIdx.y * HT + wave * NT * 16;
     const bool active = h_wave < a.H;
     const int L = row_length(a.len, t, a.W);
@@ -582,7 +596,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int t = a.T - 1 - (int)blockIdx.x;
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
     const int h_wave = (int)blockIdx.y * HT + (wave / CS) * NT * 16;
     const int cgrp = wave % CS;
     const int mcb = cgrp * MAIN_PER;                           // first main tile
@@ -620,7 +634,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
             const int head = h_wave + nt * 16 + n;
             const bool hv = head < a.H;
-            const __bf16* src = a.ws_ds + ((size_t)t * a.H + (hv ? head : 0)) * a.Wp + b * BLK + 4 * g;
+            const __bf16* src = a.ws_ds + ((size_t)(t - a.t0) * a.H + (hv ? head : 0)) * a.Wp + b * BLK + 4 * g;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (hv) {
@@ -762,7 +776,7 @@ __device__ __forceinline__ void pd_tiles_async(const BwdArgs& a, __bf16* buf, in
         const int piece = i - which * NP;
         const int h = 8 * piece + row_in;
         if (h < a.H) {
-            const __bf16* src = (which ? a.ws_ds : a.ws_p) + ((size_t)t * a.H + h) * a.Wp + b * BLK +
+            const __bf16* src = (which ? a.ws_ds : a.ws_p) + ((size_t)(t - a.t0) * a.H + h) * a.Wp + b * BLK +
                                 ((pc ^ pf(h)) << 3);
             __builtin_amdgcn_global_load_lds((const void*)src,
                                              (lds_void*)(buf + which * HP * BLK + 8 * piece * BLK), 16, 0, 0);
@@ -848,7 +862,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int t = a.T - 1 - (int)blockIdx.x;
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
     if (nblk == 0) return;                 // uniform: an empty row adds nothing
@@ -936,7 +950,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
     // slot 16 qt + n, columns c_wave + 16 nt + 4g .. +3
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<char*>(a.partial) + (size_t)t * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
+        reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
         0x00020000);
     const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 4 * (lane >> 4));
     for (int b = 0; b < nblk; b += 2) {
@@ -1018,6 +1032,11 @@ __global__ __launch_bounds__(256) void dkv_combine_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63;
     if (r >= a.S_kv) return;
     const int p0 = a.part_off[r], p1 = a.part_off[r + 1];
+    // the first chunk writes every row (0 where no slot of it names the row);
+    // a later chunk adds its sum to the rows it names, so a row's total is
+    // summed chunk by chunk in token order
+    const bool first = a.t0 == 0;
+    if (!first && p0 == p1) return;
     f32x4 acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = zero4();
@@ -1031,7 +1050,10 @@ __global__ __launch_bounds__(256) void dkv_combine_kernel(BwdArgs a) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int c = 4 * (lane + 64 * v);
-        if (c < DQK) *reinterpret_cast<f32x4*>(a.dkv + (size_t)r * DQK + c) = acc[v];
+        if (c < DQK) {
+            f32x4* dst = reinterpret_cast<f32x4*>(a.dkv + (size_t)r * DQK + c);
+            *dst = first ? acc[v] : *dst + acc[v];
+        }
     }
 }
 
@@ -1065,30 +1087,64 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
     if (threadIdx.x == 0) d_sink[h] = -s_part[0];
 }
 
-template <int DQK, int HK>
-static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.T), dim3(512), 0, stream, a);
+// stage boundaries: 0 start | 1 index inversion | 2 sdp | 3 dq | 4 dkv |
+// 5 reduce | 6 d_sink.  With several token chunks, events 1-5 are recorded
+// during the first chunk only (they bracket its stages) and event 6 after the
+// whole call.
+struct Marks {
+    hipEvent_t* ev;
+    hipStream_t stream;
+    hipError_t* err;
+    bool on;
+    __host__ void operator()(int i) const {
+        if (ev == nullptr || !on) return;
+        const hipError_t e = hipEventRecord(ev[i], stream);
+        if (*err == hipSuccess) *err = e;
+    }
+};
+
+// The index inversion of the chunk in a (rows of every range, token order).
+static hipError_t launch_inversion(const BwdArgs& a, hipStream_t stream) {
+    const int nr = a.S_kv < INV_ROWS ? a.S_kv : INV_ROWS;
+    const size_t lds = (size_t)nr * sizeof(int);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err == hipSuccess)
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_fill_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    const dim3 grid(a.nsub, (a.S_kv + INV_ROWS - 1) / INV_ROWS);
+    hipLaunchKernelGGL(rows_count_kernel, grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 31) / 32), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL(rows_parts_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(rows_fill_kernel, grid, dim3(256), lds, stream, a);
+    return hipSuccess;
 }
 
+template <int DQK, int HK>
+static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.Tc), dim3(512), 0, stream, a);
+}
+
+// One token chunk: inversion, S/P/dP/dS, dQ, dKV partials, reduce into dkv.
 template <int DQK>
-static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev, hipError_t& err) {
-    auto mark = [&](int i) {
-        if (ev == nullptr) return;
-        const hipError_t e = hipEventRecord(ev[i], stream);
-        if (err == hipSuccess) err = e;
-    };
+static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Marks& mark) {
+    const hipError_t err = launch_inversion(a, stream);
+    if (err != hipSuccess) return err;
+    mark(1);
     const int hk = (a.H + 31) / 32;
     // sdp: 16 heads per wave keep q and dO (the B operands) within half the
     // register file, so two waves share each SIMD and hide each other's
     // gather and LDS latency; 8 such waves cover 128 heads.
     if (a.H > 64) {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.T, 1), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.Tc, 1), dim3(512), 0, stream, a);
         mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.T, 1), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.Tc, 1), dim3(512), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.Tc, 1), dim3(256), 0, stream, a);
         mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.T, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.Tc, 1), dim3(256), 0, stream, a);
     }
     mark(3);
     switch (hk) {
@@ -1101,12 +1157,14 @@ static void launch_bwd_t(const BwdArgs& a, hipStream_t stream, hipEvent_t* ev, h
     hipLaunchKernelGGL((dkv_part_kernel<DQK>), dim3((a.max_parts + 3) / 4), dim3(256), 0, stream, a);
     hipLaunchKernelGGL((dkv_combine_kernel<DQK>), dim3((a.S_kv + 3) / 4), dim3(256), 0, stream, a);
     mark(5);
+    return hipSuccess;
 }
 
 // Exact Delta: the S / dP half of bwd_sdp, accumulating sum_j P_j dP_j
 // instead of storing P and dS.
 template <int DQK>
 static void launch_delta_exact_t(const BwdArgs& a, hipStream_t stream) {
+    // a.t0 = 0, a.Tc = T: every token
     if (a.H > 64)
         hipLaunchKernelGGL((delta_exact_kernel<DQK, 8, 1>), dim3(a.T, 1), dim3(512), 0, stream, a);
     else
@@ -1119,47 +1177,39 @@ hipError_t launch_delta_exact(int d_qk, const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(int d_qk, const BwdArgs& a, float* d_sink, hipStream_t stream,
+hipError_t launch_bwd(int d_qk, const BwdArgs& args, float* d_sink, hipStream_t stream,
                       hipEvent_t* ev) {
-    // stage boundaries: 0 start | 1 index inversion | 2 sdp | 3 dq | 4 dkv |
-    // 5 reduce | 6 d_sink
     hipError_t err = hipSuccess;
-    auto mark = [&](int i) {
-        if (ev == nullptr) return;
-        const hipError_t e = hipEventRecord(ev[i], stream);
-        if (err == hipSuccess) err = e;
-    };
+    Marks mark{ev, stream, &err, true};
     mark(0);
-    if (a.T > 0) {
-        const int nch = (a.T + a.tchunk - 1) / a.tchunk;
-        const size_t lds = (size_t)a.S_kv * sizeof(int);
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err == hipSuccess)
-            err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_fill_kernel),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(rows_count_kernel, dim3(nch), dim3(256), lds, stream, a);
-        hipLaunchKernelGGL(rows_chunkscan_kernel, dim3((a.S_kv + 31) / 32), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
-        hipLaunchKernelGGL(rows_parts_kernel, dim3((a.S_kv + 255) / 256), dim3(256), 0, stream, a);
-        hipLaunchKernelGGL(rows_fill_kernel, dim3(nch), dim3(256), lds, stream, a);
-        mark(1);
-        if (d_qk == 576) launch_bwd_t<576>(a, stream, ev, err);
-        else launch_bwd_t<512>(a, stream, ev, err);
+    if (args.T > 0) {
+        // token chunks of args.Tc tokens (the last one may be shorter), in
+        // token order: the workspace holds one chunk
+        for (int t0 = 0; t0 < args.T && err == hipSuccess; t0 += args.Tc) {
+            BwdArgs a = args;
+            a.t0 = t0;
+            a.Tc = args.T - t0 < args.Tc ? args.T - t0 : args.Tc;
+            a.tchunk = (a.Tc + a.nsub - 1) / a.nsub;
+            a.nsub = (a.Tc + a.tchunk - 1) / a.tchunk;
+            mark.on = t0 == 0;
+            const hipError_t e = d_qk == 576 ? launch_chunk_t<576>(a, stream, mark)
+                                             : launch_chunk_t<512>(a, stream, mark);
+            if (err == hipSuccess) err = e;
+        }
+        mark.on = true;
     } else {
         // no tokens: dkv is all zeros
         mark(1);
-        const size_t n = (size_t)a.S_kv * d_qk;
+        const size_t n = (size_t)args.S_kv * d_qk;
         const size_t want = (n + 255) / 256;
         const int fb = (int)(want < 4096 ? want : 4096);
         hipLaunchKernelGGL(fill_i32_kernel, dim3(fb), dim3(256), 0, stream,
-                           reinterpret_cast<int*>(a.dkv), 0, n);
+                           reinterpret_cast<int*>(args.dkv), 0, n);
         mark(2); mark(3); mark(4); mark(5);
     }
-    if (a.sink != nullptr)
-        hipLaunchKernelGGL(dsink_kernel, dim3(a.H), dim3(256), 0, stream, a.lse, a.delta, a.sink,
-                           d_sink, a.T, a.H);
+    if (args.sink != nullptr)
+        hipLaunchKernelGGL(dsink_kernel, dim3(args.H), dim3(256), 0, stream, args.lse, args.delta, args.sink,
+                           d_sink, args.T, args.H);
     mark(6);
     const hipError_t le = hipGetLastError();
     return le != hipSuccess ? le : err;

@@ -32,22 +32,29 @@ struct BwdArgs {
     const float* sink;
     __bf16* dq;
     float* dkv;
-    // workspace
-    __bf16* ws_p;     // [T, H, Wp] bf16: P
-    __bf16* ws_ds;    // [T, H, Wp] bf16: scale * dS
-    int* chunk_cnt;   // [ceil(T / tchunk), S_kv]: per token chunk, slots naming each row
-    int* row_cnt;     // [S_kv]: valid slots naming each KV row
+    // workspace, sized for one chunk of Tc tokens (tokens t0 .. t0 + Tc - 1;
+    // "local" token index t - t0)
+    __bf16* ws_p;     // [Tc, H, Wp] bf16: P
+    __bf16* ws_ds;    // [Tc, H, Wp] bf16: scale * dS
+    int* chunk_cnt;   // [nsub, S_kv]: per sub-chunk of the chunk, slots naming each row
+    int* row_cnt;     // [S_kv]: valid slots of the chunk naming each KV row
     int* row_off;     // [S_kv + 1]: segment starts of the row-grouped list
-    int* entries;     // [T * W]: flat slot indices t * Wp + j, grouped by row
-    uint32_t* partial; // [T * Wp] rows of 2 * d_qk bytes: per-slot dKV contributions, 4-value blocks
+    int* entries;     // [Tc * W]: local flat slot indices (t - t0) * Wp + j, grouped by row
+    uint32_t* partial; // [Tc * Wp] rows of 2 * d_qk bytes: per-slot dKV contributions, 4-value blocks
     int* part_off;    // [S_kv + 1]: first reduce part of each row
     int* part_row;    // [max_parts]: row of each reduce part
     float* part_sum;  // [max_parts, d_qk] fp32: sums of the parts
     int max_parts;
     int T, S_kv, H, W, Wp;
-    int tchunk;       // tokens per chunk of the index inversion
+    int t0, Tc;       // the chunk: its first token and its token count
+    int nsub;         // sub-chunks of the chunk in the index inversion
+    int tchunk;       // tokens per sub-chunk
     float scale, scale_log2;
 };
+
+// Rows of the KV set whose inversion counters one workgroup keeps in LDS
+// (128 KB); larger sets are split into row ranges, one workgroup per range.
+constexpr int INV_ROWS = 32768;
 
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
 hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,

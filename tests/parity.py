@@ -41,10 +41,16 @@ def to_dev(p, dev):
     )
 
 
-def run_gpu(p, dev, nan_prefill=True):
-    """Forward + preprocess + backward on the GPU; returns host numpy arrays."""
+def run_gpu(p, dev, nan_prefill=True, ws_tokens=None):
+    """Forward + preprocess + backward on the GPU; returns host numpy arrays.
+    ``ws_tokens``: give the backward the workspace of that many tokens, so it
+    runs in token chunks of (about) that size."""
     from sparse_top_attention_topk_amd import _lib
     d = to_dev(p, dev)
+    ws = None
+    if ws_tokens is not None:
+        nb = _lib.smla_bwd_workspace_size(ws_tokens, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale)
+        ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
     T, H = p.T, p.H
     o = torch.empty((T, H, p.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -59,7 +65,7 @@ def run_gpu(p, dev, nan_prefill=True):
     if d["sink"] is not None:
         d_sink = torch.full((H,), float("nan"), dtype=torch.float32, device=dev)
     dq, dkv, d_sink = _lib.smla_bwd(d["q"], d["kv"], d["dO"], lse, delta, d["idx"], d["length"],
-                                    d["sink"], p.scale, dq=dq, dkv=dkv, d_sink=d_sink)
+                                    d["sink"], p.scale, dq=dq, dkv=dkv, d_sink=d_sink, workspace=ws)
     torch.cuda.synchronize()
     out = dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.float().cpu().numpy(),
                dkv=dkv.cpu().numpy(), delta=delta.cpu().numpy(),

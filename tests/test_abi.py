@@ -56,7 +56,8 @@ def _dims(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(d_qk=128), 3), (dict(d_v=256), 3), (dict(H=129), 3), (dict(H=0), 2),
-    (dict(S_kv=40961), 3),
+    (dict(S_kv=1864136), 3), (dict(S_kv=2097152, d_qk=512), 3), (dict(W=(1 << 24) + 1), 3),
+    (dict(S_kv=40961), 1), (dict(S_kv=1864135), 1), (dict(S_kv=2097151, d_qk=512), 1),
     (dict(W=0), 2), (dict(S_kv=0), 2), (dict(T=-1), 2), (dict(scale=float("nan")), 2),
 ])
 def test_fwd_rejects_bad_dims(lib, kw, code):
@@ -96,23 +97,37 @@ def test_empty_problem_is_a_no_op(lib):
                                         None, None) == 0
 
 
-def _ws_expected(T, S_kv, H, d_qk, W):
-    """The documented workspace layout of smla_bwd, each region 256-byte aligned."""
+def _ws_expected(C, S_kv, H, d_qk, W):
+    """The documented workspace layout of smla_bwd for chunks of C tokens,
+    each region 256-byte aligned."""
     a = lambda x: (x + 255) // 256 * 256
     Wp = (W + 63) // 64 * 64
-    pd = T * H * Wp * 2
+    pd = C * H * Wp * 2
     off = a(pd)                          # P
     off = a(off + pd)                    # scale * dS
-    tch = (T + 255) // 256 if T > 256 else 1
-    off = a(off + (T + tch - 1) // tch * S_kv * 4)   # chunk counts
+    nsub = min(256, max(1, (1 << 24) // S_kv), C)
+    off = a(off + nsub * S_kv * 4)       # sub-chunk counts
     off = a(off + S_kv * 4)              # row counts
     off = a(off + (S_kv + 1) * 4)        # row offsets
-    off = a(off + T * W * 4)             # row lists
-    off = a(off + T * Wp * d_qk * 2)     # partials (16 bits per value)
-    mp = T * W // 64 + S_kv
+    off = a(off + C * W * 4)             # row lists
+    off = a(off + C * Wp * d_qk * 2)     # partials (16 bits per value)
+    mp = C * W // 64 + min(S_kv, C * W)
     off = a(off + (S_kv + 1) * 4)        # part offsets
     off = a(off + mp * 4)                # part rows
     return a(off + mp * d_qk * 4)        # part sums
+
+
+DEFAULT_WS = 8 << 30
+
+
+def _default_chunk(T, S_kv, H, d_qk, W):
+    """Tokens per chunk for the default workspace: all T when that fits the
+    8 GiB default, else equal chunks of at most the largest size that fits."""
+    if _ws_expected(T, S_kv, H, d_qk, W) <= DEFAULT_WS:
+        return T
+    c = max(c for c in range(1, T + 1) if _ws_expected(c, S_kv, H, d_qk, W) <= DEFAULT_WS)
+    n = -(-T // c)
+    return -(-T // n)
 
 
 def test_workspace_size_and_check(lib):
@@ -128,6 +143,30 @@ def test_workspace_size_and_check(lib):
     st = lib.LIB.smla_bwd(ctypes.byref(d), p, p, p, p, p, p, None, p, p, p, None, p,
                           ctypes.c_size_t(1 << 20), None)
     assert st == 1
+
+
+def test_workspace_is_chunked_past_the_default():
+    """The T = 16384 pro shape: all tokens at once would take ~30 GB, so the
+    default workspace holds equal token chunks within 8 GiB; a headline-size
+    problem is one chunk."""
+    from sparse_top_attention_topk_amd import _lib
+    pro = (16384, 16384, 128, 512, 1152)
+    full = _ws_expected(16384, 16384, 128, 512, 1152)
+    assert full > DEFAULT_WS
+    got = _lib.smla_bwd_workspace_size(16384, 16384, 128, 512, 512, 1152)
+    C = _default_chunk(*pro)
+    assert C < 16384 and got == _ws_expected(C, 16384, 128, 512, 1152) <= DEFAULT_WS
+    head = _lib.smla_bwd_workspace_size(4096, 4096, 128, 576, 512, 640)
+    assert head == _ws_expected(4096, 4096, 128, 576, 640) < DEFAULT_WS
+
+
+def test_large_kv_sets_are_accepted(lib):
+    """More KV rows than one workgroup's LDS counters cover (the inversion
+    splits the rows into ranges): sizes are accepted and the workspace grows
+    with S_kv only through per-row arrays."""
+    d = _dims(lib, T=10, S_kv=100000, H=8, W=64)
+    assert lib.LIB.smla_bwd_workspace_size(ctypes.byref(d)) == _ws_expected(10, 100000, 8, 576, 64)
+    assert lib.LIB.smla_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None) == 1
 
 
 def test_profiled_rejects_missing_events(lib):

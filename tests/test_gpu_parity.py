@@ -267,6 +267,80 @@ def test_batched_sequences(compact):
 
 
 # ---------------------------------------------------------------------------
+# the backward in token chunks (workspace smaller than all tokens need)
+# ---------------------------------------------------------------------------
+CHUNK_CASES = {
+    "edge-compact-h24-c1": (lambda: wl.make_edge_compact(24), 1),
+    "edge-wide-h128-c7": (lambda: wl.make_edge_wide(128), 7),
+    "edge-sink-h90-c40": (lambda: wl.make_edge_sink(90), 40),
+    "batched-c100": (lambda: wl.make_batched(), 100),
+    "dsv4-512-h96-c64": (lambda: wl.make_dsv4(320, 96, 512, 512, 96, seed=76, window=64), 64),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNK_CASES))
+def test_chunked_backward(name):
+    """A workspace that holds only some tokens makes the backward run chunk by
+    chunk (index inversion, S/dP, dQ, dKV partials and reduce per chunk,
+    dKV accumulated over the chunks in token order).  The outputs meet the
+    oracle; O, LSE, Delta, dQ and d_sink are the bits of the one-chunk run,
+    dKV differs from it only by the summation grouping."""
+    make, C = CHUNK_CASES[name]
+    p = make()
+    say(f"[gpu] chunked {name}: T={p.T} S_kv={p.S_kv} H={p.H} W={p.W}, workspace of {C} tokens")
+    g = run_gpu(p, DEV, ws_tokens=C)
+    errors = compare_full(g, run_oracle(p))
+    one = run_gpu(p, DEV)
+    for k in ("o", "lse", "delta", "dq", "d_sink"):
+        if g[k] is not None and not np.array_equal(g[k], one[k]):
+            errors.append(f"{k} differs from the one-chunk run")
+    m = np.abs(one["dkv"]).max()
+    e = np.abs(g["dkv"] - one["dkv"]).max()
+    say(f"[gpu] chunked {name}: dkv vs one chunk max diff {e:.3e} (max {m:.3e})")
+    if e > 1e-5 * m:
+        errors.append(f"dkv differs from the one-chunk run by {e:.3e}")
+    assert not errors, f"{name}: " + "; ".join(errors)
+
+
+def test_batched_large_kv_set():
+    """Three sequences whose concatenated KV set (43000 rows) is larger than
+    one workgroup's inversion counters cover (32768 rows): O, LSE, dQ and
+    Delta on sampled tokens and dKV on sampled rows against the oracle,
+    d_sink over every token against the oracle's sink gradient; each
+    sequence's outputs are the bits of that sequence run alone."""
+    p = wl.make_batched(H=16, lengths=(20000, 15000, 8000), window=64, topk=64, seed=77)
+    assert p.S_kv > 40960
+    say(f"[gpu] batched large: T={p.T} S_kv={p.S_kv} H={p.H} W={p.W}")
+    gpu = run_gpu(p, DEV)
+    errors = []
+    segs = p.meta["segments"]
+    toks = np.unique(np.concatenate([[a, a + 1, b - 1] for a, b in segs] +
+                                    [np.random.default_rng(9).integers(0, p.T, 24)]))
+    ref = run_oracle(p, tokens=toks)
+    check_tensor("o[sampled]", gpu["o"][toks], ref["o"], errors)
+    check_lse(gpu["lse"][toks], ref["lse"], errors)
+    check_tensor("dq[sampled]", gpu["dq"][toks], ref["dq"], errors)
+    check_tensor("delta[sampled]", gpu["delta"][toks], ref["delta"], errors)
+    rows = np.array([a for a, _ in segs] + [b - 1 for _, b in segs] + [32767, 32768, 40000])
+    toks_r = tokens_referencing(p, rows)
+    ref_r = run_oracle(p, tokens=toks_r)
+    check_tensor("dkv[sampled rows]", gpu["dkv"][rows], ref_r["dkv"][rows], errors)
+    x = p.np_inputs()
+    ds_ref = oracle.oracle_dsink(x["q"], x["kv"], x["dO"], x["topk_idxs"], x["topk_length"], x["attn_sink"],
+                                 x["scale"], x["d_v"], delta_from="bf16")
+    check_dsink(gpu["d_sink"], ds_ref, errors)
+    named = referenced_rows(p)
+    if np.any(gpu["dkv"][~named] != 0) or not np.all(np.any(gpu["dkv"][named] != 0, axis=1)):
+        errors.append("dkv: named / unnamed row structure")
+    for i, (a, b) in enumerate(segs):
+        g = run_gpu(wl.segment(p, i), DEV)
+        for k in ("o", "lse", "dq", "dkv"):
+            if not np.array_equal(gpu[k][a:b], g[k]):
+                errors.append(f"segment {i}: {k} differs from the sequence run alone")
+    assert not errors, "; ".join(errors)
+
+
+# ---------------------------------------------------------------------------
 # exact Delta (smla_bwd_delta_exact) and the backward fed with it
 # ---------------------------------------------------------------------------
 EXACT_TOL = 1e-4
