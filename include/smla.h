@@ -37,7 +37,8 @@
  *     memory and never synchronises: work is enqueued on `stream` (a
  *     hipStream_t; NULL means the null stream) and the call returns.
  *   - Errors are reported by the return value before anything is enqueued;
- *     SMLA_ERR_LAUNCH reports a failed kernel launch.  No global state is kept.
+ *     SMLA_ERR_LAUNCH reports a failed kernel launch.  No global state is kept
+ *     (except the fixed scratch of smla_bwd_noalloc).
  *   - Outputs are fully overwritten (a NaN-prefilled output comes back fully
  *     written), including the rows of empty tokens.
  */
@@ -65,7 +66,9 @@ typedef enum {
     SMLA_ERR_UNSUPPORTED = 3, /* a size outside the supported range          */
     SMLA_ERR_ALIGN = 4,       /* a base pointer is not 16-byte aligned       */
     SMLA_ERR_WORKSPACE = 5,   /* workspace NULL or too small for one token   */
-    SMLA_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch     */
+    SMLA_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch     */
+    SMLA_ERR_SCRATCH = 7      /* smla_bwd_noalloc: problem too large for its
+                                 fixed scratch                               */
 } smla_status;
 
 /* Problem sizes.  T query tokens, S_kv KV rows, H heads, head widths d_qk and
@@ -196,6 +199,33 @@ smla_status smla_bwd_profiled(const smla_dims* dims, const void* q, const void* 
                               const float* attn_sink, void* dq, float* dkv, float* d_sink,
                               void* workspace, size_t workspace_bytes, void* stream,
                               void* const* stage_events, int n_events);
+
+/* Bytes of the fixed per-GPU scratch of smla_bwd_noalloc (256 MiB). */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* smla_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The library keeps
+ * a fixed scratch of SMLA_NOALLOC_SCRATCH_BYTES in device memory on every GPU
+ * it runs on (held until the process ends) and uses the current device's
+ * copy as smla_bwd's workspace: the tokens are processed in chunks that fit
+ * in it (for the T = 4096, H = 128, 640-slot headline about 150 tokens per
+ * chunk).  No call allocates or frees anything.
+ *
+ * Arguments, outputs and errors are those of smla_bwd (no workspace), plus
+ * SMLA_ERR_SCRATCH when even one token's chunk needs more than the scratch
+ * (very wide rows or very many KV rows).  stream must belong to the current
+ * device.  Nothing in the scratch needs to start at zero: every value read
+ * in a call is written earlier in that call.  All calls on one GPU share its
+ * scratch, so calls that overlap on one GPU (other streams, other threads)
+ * race; serialise them.  dkv's bits follow the chunk size, so they can differ
+ * from smla_bwd's with a larger workspace by the summation grouping.
+ */
+smla_status smla_bwd_noalloc(const smla_dims* dims, const void* q, const void* kv,
+                             const void* dO, const float* lse, const float* delta,
+                             const int32_t* topk_idxs, const int32_t* topk_length,
+                             const float* attn_sink, void* dq, float* dkv, float* d_sink,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* smla_status_string(smla_status status);

@@ -53,6 +53,8 @@ def _load():
                                       ctypes.c_size_t, P, ctypes.POINTER(ctypes.c_void_p),
                                       ctypes.c_int]
     lib.smla_bwd_profiled.restype = ctypes.c_int
+    lib.smla_bwd_noalloc.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P]
+    lib.smla_bwd_noalloc.restype = ctypes.c_int
     lib.smla_status_string.argtypes = [ctypes.c_int]
     lib.smla_status_string.restype = ctypes.c_char_p
     return lib
@@ -61,7 +63,9 @@ def _load():
 LIB = _load()
 
 EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
-            "smla_bwd", "smla_bwd_from_o", "smla_bwd_profiled", "smla_status_string")
+            "smla_bwd", "smla_bwd_from_o", "smla_bwd_profiled", "smla_bwd_noalloc", "smla_status_string")
+
+SMLA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 BWD_STAGES = ("index_inversion", "sdp", "dq", "dkv", "dkv_reduce", "dsink")
 
@@ -271,3 +275,35 @@ def smla_bwd_from_o(q, kv, dO, o, lse, topk_idxs, topk_length, attn_sink, scale,
 def smla_bwd_profiled(*args, stage_events, **kw):
     """smla_bwd recording ``stage_events`` at its stage boundaries."""
     return smla_bwd(*args, stage_events=stage_events, **kw)
+
+
+def smla_bwd_noalloc(q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, scale, dq=None, dkv=None,
+                     d_sink=None, stream=None):
+    """smla_bwd on the library's fixed per-GPU scratch (no workspace, nothing
+    allocated by the call when the outputs are given); returns (dq, dkv,
+    d_sink or None).  Calls that overlap on one GPU share the scratch."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(kv, "kv", torch.bfloat16, dev, 2)
+    _need(dO, "dO", torch.bfloat16, dev, 3)
+    _need(lse, "lse", torch.float32, dev, 2)
+    _need(delta, "delta", torch.float32, dev, 2)
+    _need(topk_idxs, "topk_idxs", torch.int32, dev, 2)
+    _need(topk_length, "topk_length", torch.int32, dev, 1)
+    _need(attn_sink, "attn_sink", torch.float32, dev, 1)
+    T, H, d_qk = q.shape
+    d_v = dO.shape[2]
+    dims = _dims_from(q, kv, topk_idxs, scale, d_v)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dkv is None:
+        dkv = torch.empty((kv.shape[0], d_qk), dtype=torch.float32, device=dev)
+    if attn_sink is not None and d_sink is None:
+        d_sink = torch.empty((H,), dtype=torch.float32, device=dev)
+    _need(dq, "dq", torch.bfloat16, dev, 3)
+    _need(dkv, "dkv", torch.float32, dev, 2)
+    _need(d_sink, "d_sink", torch.float32, dev, 1)
+    _check(LIB.smla_bwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta),
+                                _ptr(topk_idxs), _ptr(topk_length), _ptr(attn_sink), _ptr(dq), _ptr(dkv),
+                                _ptr(d_sink), _stream(dev, stream)), "smla_bwd_noalloc")
+    return dq, dkv, d_sink

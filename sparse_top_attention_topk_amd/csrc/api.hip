@@ -4,6 +4,15 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
+// The fixed scratch of smla_bwd_noalloc: one array per GPU, held from the
+// library's load until the process ends.  Host code never uses this name as
+// an address (on the host it is a stand-in): the device address of each GPU's
+// copy comes from hipGetSymbolAddress on that GPU and is kept in
+// g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SMLA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -96,6 +105,28 @@ int balanced_chunk(const smla_dims* d, int cmax) {
     return (int)(((int64_t)d->T + n - 1) / n);
 }
 
+constexpr int MAX_DEVICES = 64;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, looked up once per device with that
+// device current (the first smla_bwd_noalloc call on it).
+smla_status scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SMLA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return SMLA_ERR_LAUNCH;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SMLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +142,9 @@ const char* smla_status_string(smla_status s) {
         case SMLA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
         case SMLA_ERR_WORKSPACE: return "workspace missing or smaller than one token's chunk needs";
         case SMLA_ERR_LAUNCH: return "kernel launch failed";
+        case SMLA_ERR_SCRATCH:
+            return "smla_bwd_noalloc: one token's chunk of this problem needs more than the library's "
+                   "fixed scratch (SMLA_NOALLOC_SCRATCH_BYTES); use smla_bwd with a workspace";
     }
     return "unknown status";
 }
@@ -283,6 +317,21 @@ smla_status smla_bwd_profiled(const smla_dims* d, const void* q, const void* kv,
         if (stage_events[i] == nullptr) return SMLA_ERR_NULL;
     return bwd_impl(d, q, kv, dO, nullptr, lse, const_cast<float*>(delta), topk_idxs, topk_length, attn_sink,
                     dq, dkv, d_sink, workspace, workspace_bytes, stream, stage_events);
+}
+
+smla_status smla_bwd_noalloc(const smla_dims* d, const void* q, const void* kv, const void* dO,
+                             const float* lse, const float* delta, const int32_t* topk_idxs,
+                             const int32_t* topk_length, const float* attn_sink, void* dq, float* dkv,
+                             float* d_sink, void* stream) {
+    smla_status st = check_dims(d);
+    if (st != SMLA_OK) return st;
+    // the fixed scratch must hold at least one token's chunk
+    if (d->T > 0 && max_chunk(d, SMLA_NOALLOC_SCRATCH_BYTES) == 0) return SMLA_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != SMLA_OK) return st;
+    return bwd_impl(d, q, kv, dO, nullptr, lse, const_cast<float*>(delta), topk_idxs, topk_length, attn_sink,
+                    dq, dkv, d_sink, ws, SMLA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

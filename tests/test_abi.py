@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact",
                                            "smla_bwd", "smla_bwd_from_o", "smla_bwd_workspace_size",
-                                           "smla_bwd_profiled", "smla_status_string"])
+                                           "smla_bwd_profiled", "smla_bwd_noalloc", "smla_status_string"])
     from sparse_top_attention_topk_amd import _lib
     assert sorted(_lib.EXPORTED) == declared_functions()
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.LIB.smla_status_string(code)
     assert lib.LIB.smla_status_string(0) == b"ok"
 
@@ -179,3 +179,16 @@ def test_profiled_rejects_missing_events(lib):
     assert lib.LIB.smla_bwd_profiled(*args, evs, 6) == 2
     evs[3] = None
     assert lib.LIB.smla_bwd_profiled(*args, evs, 7) == 1
+
+
+def test_noalloc_rejects_before_touching_the_gpu(lib):
+    """smla_bwd_noalloc checks sizes first: unsupported dims, and a problem
+    whose one-token chunk needs more than the fixed scratch (here a row of
+    2^23 slots), are refused before any device call."""
+    p = ctypes.c_void_p(0x1000)
+    bad = _dims(lib, d_qk=128)
+    args = (p, p, p, p, p, p, None, None, p, p, None, None)
+    assert lib.LIB.smla_bwd_noalloc(ctypes.byref(bad), *args) == 3
+    wide = _dims(lib, W=1 << 23, H=128)
+    assert lib.LIB.smla_bwd_noalloc(ctypes.byref(wide), *args) == 7
+    assert b"fixed scratch" in lib.LIB.smla_status_string(7)
