@@ -1,6 +1,7 @@
 """Benchmark: sparse MLA forward + backward on one MI355X.
 
-One step = smla_fwd + smla_bwd_preprocess + smla_bwd over one batch of the
+One step = smla_fwd (smla_fwd_splitkv when few tokens make the forward split
+its blocks) + smla_bwd_preprocess + smla_bwd over one batch of the
 synthetic workload (inputs already resident in HBM).  ``value`` comes from the
 wall clock around the timed steps (plain calls); the per-stage times in
 ``detail`` from a few more steps with HIP events at the stage boundaries.  Default workload:
@@ -98,6 +99,9 @@ def run_workload(p, steps, warmup, n_event_steps=5, exact_delta=True):
     d_sink = torch.empty((p.H,), dtype=torch.float32, device=dev) if sink is not None else None
     ws_bytes = _lib.smla_bwd_workspace_size(p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale)
     ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    # few tokens: the forward splits each token's blocks (none at the headline)
+    fws_bytes = _lib.smla_fwd_splitkv_workspace_size(p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale)
+    fws = torch.empty((max(fws_bytes, 16),), dtype=torch.uint8, device=dev) if fws_bytes else None
     stream = torch.cuda.current_stream(dev)   # the library launches on this stream
 
     # events: [fwd start, fwd end = preprocess start, preprocess end = bwd stage 0, bwd stages...]
@@ -112,7 +116,10 @@ def run_workload(p, steps, warmup, n_event_steps=5, exact_delta=True):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        _lib.smla_fwd(q, kv, idx, length, sink, p.scale, o=o, lse=lse, stream=stream)
+        if fws is None:
+            _lib.smla_fwd(q, kv, idx, length, sink, p.scale, o=o, lse=lse, stream=stream)
+        else:
+            _lib.smla_fwd_splitkv(q, kv, idx, length, sink, p.scale, o=o, lse=lse, workspace=fws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         _lib.smla_bwd_preprocess(o, dO, delta=delta, stream=stream)
@@ -138,7 +145,7 @@ def run_workload(p, steps, warmup, n_event_steps=5, exact_delta=True):
         step(ev)
     torch.cuda.synchronize()
 
-    out = {"ms_per_step": wall * 1e3 / steps, "ws_bytes": ws_bytes}
+    out = {"ms_per_step": wall * 1e3 / steps, "ws_bytes": ws_bytes, "fwd_ws_bytes": fws_bytes}
     names = ["fwd", "preprocess"] + list(_lib.BWD_STAGES)
     out["stage_ms"] = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                        for i, nm in enumerate(names)}

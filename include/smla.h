@@ -95,6 +95,29 @@ smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
                      const int32_t* topk_idxs, const int32_t* topk_length,
                      const float* attn_sink, void* o, float* lse, void* stream);
 
+/* Bytes of device workspace with which smla_fwd_splitkv splits each token's
+ * slot blocks over several workgroups: non-zero when the tokens alone (one
+ * workgroup per token and group of 64 or 128 heads) give fewer than 256
+ * workgroups, i.e. decode and short chunks against long top-k rows; 0 when
+ * no split is made (then smla_fwd_splitkv is smla_fwd). */
+size_t smla_fwd_splitkv_workspace_size(const smla_dims* dims);
+
+/* The forward with split KV [cuDNN-FE #785 review thread: the SM90 tile
+ * scheduler's grid of (blocks, heads x splits, batch)]: the 64-slot blocks
+ * of a token are cut into up to ceil(W / 64) contiguous ranges, each run by
+ * its own workgroup, which keeps the unnormalised O and its softmax sums in
+ * workspace; a second kernel merges the ranges, folds the sink and writes O
+ * and LSE exactly as smla_fwd defines them (the bits may differ from
+ * smla_fwd's in the last places).  With a workspace smaller than
+ * smla_fwd_splitkv_workspace_size the split count is reduced to fit (none
+ * when it holds no split).  workspace: workspace_bytes of device memory,
+ * 16-byte aligned, or NULL; used by this call only.  Arguments, outputs and
+ * errors otherwise as smla_fwd. */
+smla_status smla_fwd_splitkv(const smla_dims* dims, const void* q, const void* kv,
+                             const int32_t* topk_idxs, const int32_t* topk_length,
+                             const float* attn_sink, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Backward preprocess [cuDNN-FE #785 Not addressed: Delta = O . dO, fp32
  * reduction of the bf16-stored O].
  *   o, dO      bf16 [T, H, d_v]
@@ -128,6 +151,12 @@ smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const voi
  * as well; smla_bwd reports the error.  smla_bwd accepts any larger or
  * smaller workspace down to one token's need and sizes its chunks to it. */
 size_t smla_bwd_workspace_size(const smla_dims* dims);
+
+/* Tokens per chunk that smla_bwd uses with a workspace of workspace_bytes
+ * (the largest chunk whose workspace fits, evened out over the chunks when
+ * that fits too); 0 if not even one token's chunk fits (smla_bwd then
+ * returns SMLA_ERR_WORKSPACE) or the sizes are unsupported. */
+int smla_bwd_chunk_tokens(const smla_dims* dims, size_t workspace_bytes);
 
 /* Backward of L = sum(dO * O) [cuDNN-FE #785 Summary 1-3, Why 1-3;
  * cuDNN-FE #298].  Recomputes the probabilities from the forward's LSE and

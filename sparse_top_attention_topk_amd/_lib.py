@@ -37,12 +37,18 @@ def _load():
     D = ctypes.POINTER(SmlaDims)
     lib.smla_fwd.argtypes = [D, P, P, I32P, I32P, F32P, P, F32P, P]
     lib.smla_fwd.restype = ctypes.c_int
+    lib.smla_fwd_splitkv_workspace_size.argtypes = [D]
+    lib.smla_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.smla_fwd_splitkv.argtypes = [D, P, P, I32P, I32P, F32P, P, F32P, P, ctypes.c_size_t, P]
+    lib.smla_fwd_splitkv.restype = ctypes.c_int
     lib.smla_bwd_preprocess.argtypes = [D, P, P, F32P, P]
     lib.smla_bwd_preprocess.restype = ctypes.c_int
     lib.smla_bwd_delta_exact.argtypes = [D, P, P, P, F32P, I32P, I32P, F32P, F32P, P]
     lib.smla_bwd_delta_exact.restype = ctypes.c_int
     lib.smla_bwd_workspace_size.argtypes = [D]
     lib.smla_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.smla_bwd_chunk_tokens.argtypes = [D, ctypes.c_size_t]
+    lib.smla_bwd_chunk_tokens.restype = ctypes.c_int
     lib.smla_bwd.argtypes = [D, P, P, P, F32P, F32P, I32P, I32P, F32P, P, F32P, F32P, P,
                              ctypes.c_size_t, P]
     lib.smla_bwd.restype = ctypes.c_int
@@ -62,8 +68,8 @@ def _load():
 
 LIB = _load()
 
-EXPORTED = ("smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
-            "smla_bwd", "smla_bwd_from_o", "smla_bwd_profiled", "smla_bwd_noalloc", "smla_status_string")
+EXPORTED = ("smla_fwd", "smla_fwd_splitkv_workspace_size", "smla_fwd_splitkv", "smla_bwd_preprocess", "smla_bwd_delta_exact", "smla_bwd_workspace_size",
+            "smla_bwd_chunk_tokens", "smla_bwd", "smla_bwd_from_o", "smla_bwd_profiled", "smla_bwd_noalloc", "smla_status_string")
 
 SMLA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
@@ -136,6 +142,46 @@ def smla_fwd(q, kv, topk_idxs, topk_length, attn_sink, scale, o=None, lse=None, 
     return o, lse
 
 
+def smla_fwd_splitkv_workspace_size(T, S_kv, H, d_qk, d_v, W, scale=1.0) -> int:
+    dims = make_dims(T, S_kv, H, d_qk, d_v, W, scale)
+    return int(LIB.smla_fwd_splitkv_workspace_size(ctypes.byref(dims)))
+
+
+def smla_fwd_splitkv(q, kv, topk_idxs, topk_length, attn_sink, scale, o=None, lse=None, workspace=None,
+                     stream=None, d_v=512):
+    """Forward with the token's slot blocks split over several workgroups
+    when few tokens would leave the GPU idle; returns (o, lse) as smla_fwd.
+    ``workspace``: uint8 device tensor, or None to allocate
+    smla_fwd_splitkv_workspace_size bytes here."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 3)
+    _need(kv, "kv", torch.bfloat16, dev, 2)
+    _need(topk_idxs, "topk_idxs", torch.int32, dev, 2)
+    _need(topk_length, "topk_length", torch.int32, dev, 1)
+    _need(attn_sink, "attn_sink", torch.float32, dev, 1)
+    T, H, _ = q.shape
+    if topk_idxs.shape[0] != T or (topk_length is not None and topk_length.shape[0] != T):
+        raise ValueError("topk_idxs / topk_length must have T rows")
+    if attn_sink is not None and attn_sink.shape[0] != H:
+        raise ValueError("attn_sink must have H entries")
+    if o is None:
+        o = torch.empty((T, H, d_v), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.bfloat16, dev, 3)
+    _need(lse, "lse", torch.float32, dev, 2)
+    dims = _dims_from(q, kv, topk_idxs, scale, d_v)
+    if workspace is None:
+        need = int(LIB.smla_fwd_splitkv_workspace_size(ctypes.byref(dims)))
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev, 1)
+    _check(LIB.smla_fwd_splitkv(ctypes.byref(dims), _ptr(q), _ptr(kv), _ptr(topk_idxs), _ptr(topk_length),
+                                _ptr(attn_sink), _ptr(o), _ptr(lse), _ptr(workspace),
+                                ctypes.c_size_t(workspace.numel()), _stream(dev, stream)),
+           "smla_fwd_splitkv")
+    return o, lse
+
+
 def smla_bwd_preprocess(o, dO, delta=None, stream=None, scale=1.0):
     """Delta = rowsum(o * dO) in fp32; returns delta [T,H]."""
     dev = o.device
@@ -185,6 +231,11 @@ def smla_bwd_delta_exact(q, kv, dO, lse, topk_idxs, topk_length, attn_sink, scal
 def smla_bwd_workspace_size(T, S_kv, H, d_qk, d_v, W, scale=1.0) -> int:
     dims = make_dims(T, S_kv, H, d_qk, d_v, W, scale)
     return int(LIB.smla_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def smla_bwd_chunk_tokens(T, S_kv, H, d_qk, d_v, W, workspace_bytes, scale=1.0) -> int:
+    dims = make_dims(T, S_kv, H, d_qk, d_v, W, scale)
+    return int(LIB.smla_bwd_chunk_tokens(ctypes.byref(dims), ctypes.c_size_t(int(workspace_bytes))))
 
 
 def smla_bwd(q, kv, dO, lse, delta, topk_idxs, topk_length, attn_sink, scale, dq=None, dkv=None,

@@ -55,10 +55,29 @@ int inversion_subchunks(const smla_dims* d, int C) {
 //   part_off         int32 [S_kv + 1]; part_row int32 [max_parts]
 //   part_sum         fp32 [max_parts, d_qk], max_parts = C * W / 64 + min(S_kv, C * W)
 //                    (a row named n times has ceil(n / 64) parts)
+//   dq_part          fp32 [C, nsplit, H, d_qk] when the blocks are split (C < 256)
 struct WsLayout {
-    size_t p, ds, chunk, cnt, off, ent, part, poff, prow, psum, total;
-    int max_parts, nsub;
+    size_t p, ds, chunk, cnt, off, ent, part, poff, prow, psum, dqp, total;
+    int max_parts, nsub, nsplit, bps;
 };
+
+// Splits of each token's slot blocks in the backward for chunks of C
+// tokens: one workgroup per token fills the GPU from 256 tokens on; below,
+// the blocks are split until there are about 512 workgroups (at most one
+// split per block).
+void bwd_split_for(const smla_dims* d, int C, int* nsplit, int* bps) {
+    const int64_t nb = ((int64_t)d->W + smla::BLK - 1) / smla::BLK;
+    int64_t s = C >= 256 ? 1 : (512 + C - 1) / C;
+    if (s > nb) s = nb;
+    if (s < 2) {
+        *nsplit = 1;
+        *bps = (int)nb;
+        return;
+    }
+    const int64_t b = (nb + s - 1) / s;
+    *bps = (int)b;
+    *nsplit = (int)((nb + b - 1) / b);
+}
 
 WsLayout ws_layout(const smla_dims* d, int C) {
     WsLayout L;
@@ -78,31 +97,75 @@ WsLayout ws_layout(const smla_dims* d, int C) {
     L.max_parts = (int)mp;
     L.prow = align256(L.poff + ((size_t)d->S_kv + 1) * sizeof(int32_t));
     L.psum = align256(L.prow + mp * sizeof(int32_t));
-    L.total = align256(L.psum + mp * d->d_qk * sizeof(float));
+    L.dqp = align256(L.psum + mp * d->d_qk * sizeof(float));
+    bwd_split_for(d, C, &L.nsplit, &L.bps);
+    const size_t dqp = L.nsplit > 1 ? (size_t)C * L.nsplit * d->H * d->d_qk * sizeof(float) : 0;
+    L.total = align256(L.dqp + dqp);
     return L;
+}
+
+// ---- split forward: how many splits over each token's slot blocks.  A
+// token takes one workgroup per head tile; with few tokens the GPU's 256
+// CUs are not filled, so the blocks are split until there are about 512
+// workgroups (at most one split per block).
+struct FwdSplit {
+    int nsplit, bps, nb;
+};
+
+FwdSplit fwd_split_for(const smla_dims* d) {
+    const int64_t nb = ((int64_t)d->W + smla::BLK - 1) / smla::BLK;
+    const int ht = smla::fwd_head_tile(d->H);
+    const int64_t wgs = (int64_t)d->T * ((d->H + ht - 1) / ht);
+    int64_t s = wgs >= 256 ? 1 : (512 + wgs - 1) / wgs;
+    if (s > nb) s = nb;
+    if (s < 2) return {1, (int)nb, (int)nb};
+    const int64_t bps = (nb + s - 1) / s;
+    return {(int)((nb + bps - 1) / bps), (int)bps, (int)nb};
+}
+
+size_t fwd_split_bytes(const smla_dims* d, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t rows = (size_t)d->T * nsplit * d->H;
+    return align256(rows * 512 * sizeof(float)) + align256(rows * 4 * sizeof(float));
 }
 
 // Largest chunk whose workspace fits in `bytes` (0 if not even one token's
 // does).  Local slot indices (t - t0) * Wp + j and part counts stay in int32.
+// The workspace grows with the chunk from 256 tokens on (no block split);
+// below 256 it also holds the dQ shares of the split blocks, whose size is
+// not monotone in the chunk, so that range is scanned.
 int max_chunk(const smla_dims* d, size_t bytes) {
     const int64_t Wp = (int64_t)round_up_blk(d->W);
     int64_t hi = d->T;
     const int64_t lim = (INT32_MAX / 2) / Wp;
     if (hi > lim) hi = lim;
-    if (hi < 1 || ws_layout(d, 1).total > bytes) return 0;
-    int64_t lo = 1;                    // fits
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) / 2;
-        if (ws_layout(d, (int)mid).total <= bytes) lo = mid;
-        else hi = mid - 1;
+    if (hi < 1) return 0;
+    if (ws_layout(d, (int)hi).total <= bytes) return (int)hi;
+    if (hi > 256 && ws_layout(d, 256).total <= bytes) {
+        int64_t lo = 256;                  // fits; hi does not
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) / 2;
+            if (ws_layout(d, (int)mid).total <= bytes) lo = mid;
+            else hi = mid;
+        }
+        return (int)lo;
     }
-    return (int)lo;
+    for (int64_t c = hi < 255 ? hi : 255; c >= 1; --c)
+        if (ws_layout(d, (int)c).total <= bytes) return (int)c;
+    return 0;
 }
 
-// The same number of chunks with their sizes balanced.
-int balanced_chunk(const smla_dims* d, int cmax) {
+// Tokens per chunk for a workspace of `bytes`: the largest chunk that fits,
+// evened out over the same number of chunks when the even size fits too (it
+// may not: below 256 tokens a smaller chunk can need more, for the dQ shares
+// of its split blocks).  0 if not even one token's chunk fits.  The result
+// always satisfies ws_layout(d, C).total <= bytes.
+int chunk_tokens(const smla_dims* d, size_t bytes) {
+    const int cmax = max_chunk(d, bytes);
+    if (cmax == 0) return 0;
     const int64_t n = ((int64_t)d->T + cmax - 1) / cmax;
-    return (int)(((int64_t)d->T + n - 1) / n);
+    const int even = (int)(((int64_t)d->T + n - 1) / n);
+    return ws_layout(d, even).total <= bytes ? even : cmax;
 }
 
 constexpr int MAX_DEVICES = 64;
@@ -149,15 +212,30 @@ const char* smla_status_string(smla_status s) {
     return "unknown status";
 }
 
-smla_status smla_fwd(const smla_dims* d, const void* q, const void* kv, const int32_t* topk_idxs,
-                     const int32_t* topk_length, const float* attn_sink, void* o, float* lse,
-                     void* stream) {
+static smla_status fwd_impl(const smla_dims* d, const void* q, const void* kv, const int32_t* topk_idxs,
+                            const int32_t* topk_length, const float* attn_sink, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
     smla_status st = check_dims(d);
     if (st != SMLA_OK) return st;
     if (d->T == 0) return SMLA_OK;
     if (!q || !kv || !topk_idxs || !o || !lse) return SMLA_ERR_NULL;
     if (!aligned16(q) || !aligned16(kv) || !aligned16(o)) return SMLA_ERR_ALIGN;
-    smla::FwdArgs a;
+    if (workspace != nullptr && !aligned16(workspace)) return SMLA_ERR_ALIGN;
+    smla::FwdArgs a = {};
+    // split over the slot blocks as far as the workspace allows
+    FwdSplit sp = workspace != nullptr ? fwd_split_for(d) : FwdSplit{1, 0, 0};
+    while (sp.nsplit > 1 && fwd_split_bytes(d, sp.nsplit) > workspace_bytes) {
+        const int s = sp.nsplit - 1;             // fewer splits, as even as the blocks allow
+        sp.bps = (sp.nb + s - 1) / s;
+        sp.nsplit = (sp.nb + sp.bps - 1) / sp.bps;
+    }
+    a.nsplit = sp.nsplit > 1 ? sp.nsplit : 1;
+    a.bps = sp.bps;
+    if (a.nsplit > 1) {
+        const size_t rows = (size_t)d->T * a.nsplit * d->H;
+        a.opart = static_cast<float*>(workspace);
+        a.spart = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * 512 * sizeof(float)));
+    }
     a.q = static_cast<const __bf16*>(q);
     a.kv = static_cast<const __bf16*>(kv);
     a.idx = topk_idxs;
@@ -169,6 +247,25 @@ smla_status smla_fwd(const smla_dims* d, const void* q, const void* kv, const in
     a.scale_log2 = d->scale * smla::LOG2E;
     hipError_t e = smla::launch_fwd(d->d_qk, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+smla_status smla_fwd(const smla_dims* d, const void* q, const void* kv, const int32_t* topk_idxs,
+                     const int32_t* topk_length, const float* attn_sink, void* o, float* lse,
+                     void* stream) {
+    return fwd_impl(d, q, kv, topk_idxs, topk_length, attn_sink, o, lse, nullptr, 0, stream);
+}
+
+size_t smla_fwd_splitkv_workspace_size(const smla_dims* d) {
+    if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
+    return fwd_split_bytes(d, fwd_split_for(d).nsplit);
+}
+
+smla_status smla_fwd_splitkv(const smla_dims* d, const void* q, const void* kv, const int32_t* topk_idxs,
+                             const int32_t* topk_length, const float* attn_sink, void* o, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace == nullptr) workspace_bytes = 0;
+    return fwd_impl(d, q, kv, topk_idxs, topk_length, attn_sink, o, lse,
+                    workspace_bytes > 0 ? workspace : nullptr, workspace_bytes, stream);
 }
 
 smla_status smla_bwd_preprocess(const smla_dims* d, const void* o, const void* dO, float* delta,
@@ -219,9 +316,13 @@ size_t smla_bwd_workspace_size(const smla_dims* d) {
     const int whole = max_chunk(d, ws_layout(d, d->T).total);
     if (whole == d->T && ws_layout(d, d->T).total <= SMLA_BWD_DEFAULT_WORKSPACE)
         return ws_layout(d, d->T).total;
-    int c = max_chunk(d, SMLA_BWD_DEFAULT_WORKSPACE);
-    if (c == 0) c = 1;
-    return ws_layout(d, balanced_chunk(d, c)).total;
+    const int c = chunk_tokens(d, SMLA_BWD_DEFAULT_WORKSPACE);
+    return ws_layout(d, c > 0 ? c : 1).total;
+}
+
+int smla_bwd_chunk_tokens(const smla_dims* d, size_t workspace_bytes) {
+    if (check_dims(d) != SMLA_OK || d->T == 0) return 0;
+    return chunk_tokens(d, workspace_bytes);
 }
 
 // o == NULL: delta is an input (from the preprocess or the exact pass).
@@ -246,9 +347,9 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
     // tokens per chunk: as many as the workspace given holds (balanced)
     int C = 1;
     if (d->T > 0) {
-        C = max_chunk(d, workspace_bytes);
-        if (C == 0) return SMLA_ERR_WORKSPACE;
-        C = balanced_chunk(d, C);
+        C = chunk_tokens(d, workspace_bytes);
+        // every region the kernels address lies inside the workspace given
+        if (C == 0 || ws_layout(d, C).total > workspace_bytes) return SMLA_ERR_WORKSPACE;
     }
     smla::BwdArgs a = {};
     a.q = static_cast<const __bf16*>(q);
@@ -282,6 +383,9 @@ static smla_status bwd_impl(const smla_dims* d, const void* q, const void* kv, c
     a.part_row = reinterpret_cast<int*>(ws + WL.prow);
     a.part_sum = reinterpret_cast<float*>(ws + WL.psum);
     a.max_parts = WL.max_parts;
+    a.nsplit = WL.nsplit;
+    a.bps = WL.bps;
+    a.dq_part = WL.nsplit > 1 ? reinterpret_cast<float*>(ws + WL.dqp) : nullptr;
     a.scale = d->scale;
     a.scale_log2 = d->scale * smla::LOG2E;
     hipError_t e = smla::launch_bwd(d->d_qk, a, d_sink, static_cast<hipStream_t>(stream),

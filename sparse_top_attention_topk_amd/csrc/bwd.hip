@@ -268,11 +268,25 @@ struct NoPost {
     __device__ void operator()() const {}
 };
 
+// The blocks a workgroup of the split kernels runs: [b_lo, ...) with slots
+// below j_hi (the whole row without a split).
+struct BlockRange {
+    int b_lo, j_hi;
+};
+
+__device__ __forceinline__ BlockRange block_range(const BwdArgs& a, int L) {
+    if (a.nsplit <= 1) return {0, L};
+    const int b_lo = (int)blockIdx.z * a.bps;
+    const int j_end = (b_lo + a.bps) * BLK;
+    return {b_lo, L < j_end ? L : j_end};
+}
+
 template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
                                                 int (*s_rows)[BLK], int* s_live, int* s_last, int t, int L, int nblk,
-                                                int wave, int lane, Body&& body, Pre&& pre = Pre{},
+                                                BlockRange rg, int wave, int lane, Body&& body, Pre&& pre = Pre{},
                                                 Post&& post = Post{}) {
+    const int b_lo = rg.b_lo, j_hi = rg.j_hi;
     using Tile = KvTileSwz<DQK>;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -284,14 +298,14 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     {
         constexpr int NTH = NW * 64;
         int last = -1;
-        for (int j0 = 0; j0 < L; j0 += 4 * NTH) {
+        for (int j0 = b_lo * BLK; j0 < j_hi; j0 += 4 * NTH) {
             int v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) v[k] = raw_index_b(a, t, j0 + k * NTH + tid);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int j = j0 + k * NTH + tid;
-                if (valid_row_b(v[k], j, L, a.S_kv) >= 0) last = j;
+                if (valid_row_b(v[k], j, j_hi, a.S_kv) >= 0) last = j;
             }
         }
 #pragma unroll
@@ -299,8 +313,8 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         if (lane == 0) s_last[wave] = last;
     }
     if (tid < BLK) {
-        put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, L, a.S_kv, tid), tid);
-        put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid), tid);
+        put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, j_hi, a.S_kv, b_lo * BLK + tid), tid);
+        put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, j_hi, a.S_kv, (b_lo + 1) * BLK + tid), tid);
         put_rows(s_rows[2], &s_live[2], -1, tid);        // written again before any block reads it
     }
     __syncthreads();
@@ -308,10 +322,10 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
 #pragma unroll
     for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
     const int nbr = nblk;                                   // blocks of the row
-    nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1);
+    nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1 - b_lo);   // blocks of the range
     if (nbr > 0) {
         if (nblk > 0) {
-            pre(0, P0{});
+            pre(b_lo, P0{});
             Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
         }
         post();
@@ -325,25 +339,25 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     for (int b = 0; b < nblk; b += 2) {
         wait_vmem();
         if (b > 0 && b + 1 < nblk && tid < BLK)
-            put_rows(s_rows[(b + 1) % 3], &s_live[(b + 1) % 3], valid_row_b(ahead, (b + 1) * BLK + tid, L, a.S_kv),
-                     tid);
+            put_rows(s_rows[(b + 1) % 3], &s_live[(b + 1) % 3],
+                     valid_row_b(ahead, (b_lo + b + 1) * BLK + tid, j_hi, a.S_kv), tid);
         __syncthreads();
-        ahead = tid < BLK ? raw_index_b(a, t, (b + 2) * BLK + tid) : 0;
+        ahead = tid < BLK ? raw_index_b(a, t, (b_lo + b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < nblk) pre(b + 1, P1{});
-        body(s_tile0, s_rows[b % 3], b, P0{},
+        if (b + 1 < nblk) pre(b_lo + b + 1, P1{});
+        body(s_tile0, s_rows[b % 3], b_lo + b, P0{},
              GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane, a.S_kv, b + 1 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[b % 3]) != 0);
         if (b + 1 >= nblk) break;
         wait_vmem();
         if (b + 2 < nblk && tid < BLK)
-            put_rows(s_rows[(b + 2) % 3], &s_live[(b + 2) % 3], valid_row_b(ahead, (b + 2) * BLK + tid, L, a.S_kv),
-                     tid);
+            put_rows(s_rows[(b + 2) % 3], &s_live[(b + 2) % 3],
+                     valid_row_b(ahead, (b_lo + b + 2) * BLK + tid, j_hi, a.S_kv), tid);
         __syncthreads();
-        ahead = tid < BLK ? raw_index_b(a, t, (b + 3) * BLK + tid) : 0;
+        ahead = tid < BLK ? raw_index_b(a, t, (b_lo + b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) pre(b + 2, P0{});
-        body(s_tile1, s_rows[(b + 1) % 3], b + 1, P1{},
+        if (b + 2 < nblk) pre(b_lo + b + 2, P0{});
+        body(s_tile1, s_rows[(b + 1) % 3], b_lo + b + 1, P1{},
              GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane, a.S_kv, b + 2 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[(b + 1) % 3]) != 0);
     }
@@ -541,7 +555,8 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
     const typename Tile::Lane TL = Tile::lane_bases(lane);
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, wave, lane,
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
+                             wave, lane,
                              [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
                                  if (active && live)
                                      sdp_block<DQK, NW, NT, EXACT>(a, tile, TL, rows, qop, dop, lse2, dlt,
@@ -648,7 +663,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
         }
     };
 
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, wave, lane,
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
+                             wave, lane,
                              [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs, bool live) {
         (void)rows;
         (void)b;
@@ -674,6 +690,21 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     }, load_ds);
 
     if (!active) return;
+    if (a.nsplit > 1) {
+        // this split's share of dQ, in fp32, for dq_reduce_kernel
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            if (head >= a.H) continue;
+            float* dp = a.dq_part + (((size_t)(t - a.t0) * a.nsplit + blockIdx.z) * a.H + head) * DQK + 4 * g;
+#pragma unroll
+            for (int mc = 0; mc < MCW; ++mc) {
+                const int col = mc < MAIN_PER ? 16 * (mcb + mc) : 16 * (Tile::MC_MAIN + rpb + mc - MAIN_PER);
+                *reinterpret_cast<f32x4*>(dp + col) = acc[mc][nt];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int head = h_wave + nt * 16 + n;
@@ -684,6 +715,22 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
             const int col = mc < MAIN_PER ? 16 * (mcb + mc) : 16 * (Tile::MC_MAIN + rpb + mc - MAIN_PER);
             st4(dqp + col, cvt4(acc[mc][nt][0], acc[mc][nt][1], acc[mc][nt][2], acc[mc][nt][3]));
         }
+    }
+}
+
+// dQ of a split backward: the splits' fp32 shares summed in split order, one
+// wave per (token, head), rounded to bf16.
+template <int DQK>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
+    const int row = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= a.Tc * a.H) return;
+    const int tl = row / a.H, h = row - tl * a.H;
+    for (int c = 4 * lane; c < DQK; c += 256) {
+        f32x4 acc = zero4();
+        for (int s = 0; s < a.nsplit; ++s)
+            acc += *reinterpret_cast<const f32x4*>(a.dq_part + (((size_t)tl * a.nsplit + s) * a.H + h) * DQK + c);
+        st4(a.dq + ((size_t)(a.t0 + tl) * a.H + h) * DQK + c, cvt4(acc[0], acc[1], acc[2], acc[3]));
     }
 }
 
@@ -864,8 +911,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
     const int L = row_length(a.len, t, a.W);
+    // the row's blocks [b_lo, b_end) (all of them without a split)
     const int nblk = (L + BLK - 1) / BLK;
-    if (nblk == 0) return;                 // uniform: an empty row adds nothing
+    const int b_lo = a.nsplit > 1 ? (int)blockIdx.z * a.bps : 0;
+    const int b_end = a.nsplit > 1 && b_lo + a.bps < nblk ? b_lo + a.bps : nblk;
+    if (b_end <= b_lo) return;             // uniform: an empty row (or range) adds nothing
     // wave w owns tiles [tile0, tile0 + ntc): the first R waves NTC tiles, the
     // rest NTC - 1 (their last tile slot is computed on zero operands and not
     // stored)
@@ -905,8 +955,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     // in issue order)
     static_assert((32 * (DV / 8) / 64) / NW >= 4, "the ring waits assume at least 4 loads per piece");
     __syncthreads();                      // zero-fill done before any tile load lands
-    pd_tiles_async<HP, NW>(a, s_pd0, t, 0, wave, lane);
-    if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, 0, lane);
+    pd_tiles_async<HP, NW>(a, s_pd0, t, b_lo, wave, lane);
+    if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b_lo, lane);
     issue(0);
     if (NPC > 1) issue(1);
 #pragma unroll
@@ -953,18 +1003,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
         0x00020000);
     const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 4 * (lane >> 4));
-    for (int b = 0; b < nblk; b += 2) {
+    for (int b = b_lo; b < b_end; b += 2) {
         wait_vmem();
         __syncthreads();
-        if (b + 1 < nblk) {
+        if (b + 1 < b_end) {
             pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
         }
         dkv_block<DQK, HK, NTC>(a, s_pd0, s_raw[0], qB, dB, b, L, prs, voff, ntc, lane);
-        if (b + 1 >= nblk) break;
+        if (b + 1 >= b_end) break;
         wait_vmem();
         __syncthreads();
-        if (b + 2 < nblk) {
+        if (b + 2 < b_end) {
             pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
         }
@@ -1124,7 +1174,8 @@ static hipError_t launch_inversion(const BwdArgs& a, hipStream_t stream) {
 
 template <int DQK, int HK>
 static void launch_dkv_t(const BwdArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.Tc), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, HK>), dim3(a.Tc, 1, a.nsplit > 1 ? a.nsplit : 1), dim3(512), 0,
+                       stream, a);
 }
 
 // One token chunk: inversion, S/P/dP/dS, dQ, dKV partials, reduce into dkv.
@@ -1134,18 +1185,21 @@ static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Mar
     if (err != hipSuccess) return err;
     mark(1);
     const int hk = (a.H + 31) / 32;
+    const int ns = a.nsplit > 1 ? a.nsplit : 1;    // workgroups per token (block ranges)
     // sdp: 16 heads per wave keep q and dO (the B operands) within half the
     // register file, so two waves share each SIMD and hide each other's
     // gather and LDS latency; 8 such waves cover 128 heads.
     if (a.H > 64) {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.Tc, 1), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.Tc, 1, ns), dim3(512), 0, stream, a);
         mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.Tc, 1), dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.Tc, 1, ns), dim3(512), 0, stream, a);
     } else {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.Tc, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.Tc, 1, ns), dim3(256), 0, stream, a);
         mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.Tc, 1), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.Tc, 1, ns), dim3(256), 0, stream, a);
     }
+    if (ns > 1)
+        hipLaunchKernelGGL((dq_reduce_kernel<DQK>), dim3((a.Tc * a.H + 3) / 4), dim3(256), 0, stream, a);
     mark(3);
     switch (hk) {
         case 1: launch_dkv_t<DQK, 1>(a, stream); break;

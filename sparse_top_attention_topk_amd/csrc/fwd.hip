@@ -235,7 +235,10 @@ __device__ __forceinline__ int valid_row(int v, int j, int L, int S_kv) {
     return (j < L && v >= 0 && v < S_kv) ? v : -1;
 }
 
-template <int DQK, int NW, int NT>
+// SPLIT: the workgroup runs the blocks [b_lo, b_lo + bps) of split blockIdx.z
+// only and writes its unnormalised O^T and softmax sums to the partials
+// (merged by fwd_combine_kernel) instead of O and LSE.
+template <int DQK, int NW, int NT, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     using C = FwdCfg<DQK, NW, NT>;
     using Tile = typename C::Tile;
@@ -256,6 +259,10 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     const int h_wave = h_wg + wave * NT * 16;
     const bool active = h_wave < a.H;                 // wave-uniform
     const int L = row_length(a.len, t, a.W);
+    const int split = SPLIT ? (int)blockIdx.z : 0;
+    const int b_lo = SPLIT ? split * a.bps : 0;       // first block of this workgroup
+    // slots this workgroup may run: [b_lo * BLK, j_hi)
+    const int j_hi = SPLIT ? min(L, (b_lo + a.bps) * BLK) : L;
 
     if (tid == 0) s_rerun = 0;
 
@@ -281,14 +288,14 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     // wave's maximum goes to s_last, read after the first barrier below.
     {
         int last = -1;
-        for (int j0 = 0; j0 < L; j0 += 4 * NTH) {
+        for (int j0 = b_lo * BLK; j0 < j_hi; j0 += 4 * NTH) {
             int v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) v[k] = raw_index(a, t, j0 + k * NTH + tid);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int j = j0 + k * NTH + tid;
-                if (valid_row(v[k], j, L, a.S_kv) >= 0) last = j;
+                if (valid_row(v[k], j, j_hi, a.S_kv) >= 0) last = j;
             }
         }
 #pragma unroll
@@ -306,8 +313,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         for (int nt = 0; nt < NT; ++nt) { rmax[nt] = -INFINITY; l_run[nt] = 0.f; l_rnd[nt] = 0.f; }
 
         if (tid < BLK) {
-            s_rows[0][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, tid);
-            s_rows[1][tid] = slot_row(a.idx, t, a.W, L, a.S_kv, BLK + tid);
+            s_rows[0][tid] = slot_row(a.idx, t, a.W, j_hi, a.S_kv, b_lo * BLK + tid);
+            s_rows[1][tid] = slot_row(a.idx, t, a.W, j_hi, a.S_kv, (b_lo + 1) * BLK + tid);
             s_rows[2][tid] = -1;     // written again before any block reads it
         }
         __syncthreads();
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             int last = s_last[0];
 #pragma unroll
             for (int w = 1; w < NW; ++w) last = max(last, s_last[w]);
-            nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1);
+            nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1 - b_lo);
         }
         if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
 
@@ -331,9 +338,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             // ---- block b in tile 0
             wait_vmem();
             if (b > 0 && b + 1 < nblk && tid < BLK)
-                s_rows[(b + 1) % 3][tid] = valid_row(ahead, (b + 1) * BLK + tid, L, a.S_kv);
+                s_rows[(b + 1) % 3][tid] = valid_row(ahead, (b_lo + b + 1) * BLK + tid, j_hi, a.S_kv);
             __syncthreads();
-            ahead = tid < BLK ? raw_index(a, t, (b + 2) * BLK + tid) : 0;
+            ahead = tid < BLK ? raw_index(a, t, (b_lo + b + 2) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
             if (active)
                 fwd_block<DQK, NW, NT>(a, s_tile0, TL, s_rows[b % 3], qop, oacc, m_ref, rmax, l_run, l_rnd, lane,
@@ -344,9 +351,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
             // ---- block b+1 in tile 1
             wait_vmem();
             if (b + 2 < nblk && tid < BLK)
-                s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b + 2) * BLK + tid, L, a.S_kv);
+                s_rows[(b + 2) % 3][tid] = valid_row(ahead, (b_lo + b + 2) * BLK + tid, j_hi, a.S_kv);
             __syncthreads();
-            ahead = tid < BLK ? raw_index(a, t, (b + 3) * BLK + tid) : 0;
+            ahead = tid < BLK ? raw_index(a, t, (b_lo + b + 3) * BLK + tid) : 0;
             __builtin_amdgcn_sched_barrier(0);
             if (active)
                 fwd_block<DQK, NW, NT>(a, s_tile1, TL, s_rows[(b + 1) % 3], qop, oacc, m_ref, rmax, l_run, l_rnd,
@@ -369,6 +376,29 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) m_ref[nt] = rmax[nt];    // exact max: P <= 1
         __syncthreads();
+    }
+
+    if constexpr (SPLIT) {
+        // partials of this split: the unnormalised O^T (lane (g, n) holds
+        // columns 16 mc + 4g .. +3 of head n), and per head the reference
+        // max (log2 domain; -inf without a valid slot), the fp32 sum of the
+        // weights and the sum of their bf16 roundings
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            float l = l_run[nt], lr = l_rnd[nt];
+            l += __shfl_xor(l, 16, 64);
+            l += __shfl_xor(l, 32, 64);
+            lr += __shfl_xor(lr, 16, 64);
+            lr += __shfl_xor(lr, 32, 64);
+            if (!active || head >= a.H) continue;
+            const size_t row = ((size_t)t * a.nsplit + split) * a.H + head;
+            float* op = a.opart + row * C::DV + 4 * g;
+#pragma unroll
+            for (int mc = 0; mc < C::MC; ++mc) *reinterpret_cast<f32x4*>(op + 16 * mc) = oacc[mc][nt];
+            if (g == 0) *reinterpret_cast<f32x4*>(a.spart + row * 4) = f32x4{m_ref[nt], l, lr, 0.f};
+        }
+        return;
     }
 
     // epilogue: normalise, fold the sink, stage O^T through LDS as O rows
@@ -408,11 +438,58 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     }
 }
 
+// Merge of the split partials, one wave per (token, head): with M the largest
+// reference max among the splits that saw a valid slot and f_s = 2^(m_s - M),
+//   O = sum_s f_s O_s / sum_s f_s lr_s,   LSE = (M + log2 sum_s f_s l_s) ln 2,
+// the same normalisation (by the rounded weights) and LSE as one workgroup
+// over all blocks; then the sink fold of the forward's epilogue.
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
+    constexpr int DV = 512;
+    const int row = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= a.T * a.H) return;
+    const int t = row / a.H, h = row - t * a.H;
+    const size_t base = (size_t)t * a.nsplit * a.H + h;       // split s: base + s * H
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const f32x4 st = *reinterpret_cast<const f32x4*>(a.spart + (base + (size_t)s * a.H) * 4);
+        if (st[1] > 0.f) M = fmaxf(M, st[0]);
+    }
+    f32x4 acc0 = zero4(), acc1 = zero4();
+    float l = 0.f, lr = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < a.nsplit; ++s) {
+            const size_t r = base + (size_t)s * a.H;
+            const f32x4 st = *reinterpret_cast<const f32x4*>(a.spart + r * 4);
+            if (!(st[1] > 0.f)) continue;
+            const float f = exp2f(st[0] - M);
+            l += f * st[1];
+            lr += f * st[2];
+            const float* op = a.opart + r * DV + 8 * lane;
+            acc0 += f * *reinterpret_cast<const f32x4*>(op);
+            acc1 += f * *reinterpret_cast<const f32x4*>(op + 4);
+        }
+    }
+    const bool nonempty = l > 0.f;
+    const float lse = nonempty ? (M + log2f(l)) * LN2 : -INFINITY;
+    float f = (nonempty && lr > 0.f) ? 1.0f / lr : 0.f;
+    if (a.sink != nullptr && nonempty) f *= sigmoid(lse - a.sink[h]);
+    const bf16x8 o = cvt8(acc0 * f, acc1 * f);
+    *reinterpret_cast<u32x4*>(a.o + ((size_t)t * a.H + h) * DV + 8 * lane) = __builtin_bit_cast(u32x4, o);
+    if (lane == 0) a.lse[(size_t)t * a.H + h] = lse;
+}
+
 template <int DQK, int NW, int NT>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     constexpr int HT = NW * NT * 16;
-    dim3 grid(a.T, (a.H + HT - 1) / HT);
-    hipLaunchKernelGGL((fwd_kernel<DQK, NW, NT>), grid, dim3(NW * 64), 0, stream, a);
+    if (a.nsplit > 1) {
+        dim3 grid(a.T, (a.H + HT - 1) / HT, a.nsplit);
+        hipLaunchKernelGGL((fwd_kernel<DQK, NW, NT, true>), grid, dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL(fwd_combine_kernel, dim3((a.T * a.H + 3) / 4), dim3(256), 0, stream, a);
+    } else {
+        dim3 grid(a.T, (a.H + HT - 1) / HT);
+        hipLaunchKernelGGL((fwd_kernel<DQK, NW, NT, false>), grid, dim3(NW * 64), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -16,6 +16,11 @@ struct FwdArgs {
     float* lse;
     int T, S_kv, H, W;
     float scale_log2;   // scale * log2(e)
+    // split over each token's slot blocks (nsplit > 1): split s runs blocks
+    // [s * bps, (s + 1) * bps) and writes partials, which a combine merges
+    int nsplit, bps;
+    float* opart;       // [T, nsplit, H, 512] fp32: unnormalised O of each split
+    float* spart;       // [T, nsplit, H, 4] fp32: reference max (log2), sum, rounded sum, 0
 };
 
 struct BwdArgs {
@@ -50,6 +55,11 @@ struct BwdArgs {
     int nsub;         // sub-chunks of the chunk in the index inversion
     int tchunk;       // tokens per sub-chunk
     float scale, scale_log2;
+    // split over each token's slot blocks (nsplit > 1, few tokens): split s
+    // (blockIdx.z) of the S/dP, dQ and dKV kernels runs blocks
+    // [s * bps, (s + 1) * bps); dQ then goes through fp32 partials
+    int nsplit, bps;
+    float* dq_part;   // [Tc, nsplit, H, d_qk] fp32 when nsplit > 1
 };
 
 // Rows of the KV set whose inversion counters one workgroup keeps in LDS
@@ -57,6 +67,8 @@ struct BwdArgs {
 constexpr int INV_ROWS = 32768;
 
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
+// head tile of the forward (heads per workgroup)
+inline int fwd_head_tile(int H) { return H > 64 ? 128 : 64; }
 hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,
                              hipStream_t stream);
 // Delta[t, h] = sum_j P_j dP_j (uses q, kv, dO, lse, idx, len, sink, delta_out)

@@ -486,6 +486,28 @@ def make_spiky_dsv4(T=4096, H=128, d_qk=576, topk=512, seed=2, frac=0.10, name=N
                    p.topk_idxs, None, p.attn_sink, meta=dict(p.meta, late_spike=late))
 
 
+def make_decode(T, S_kv=16384, H=128, d_qk=576, topk=1024, window=128, seed=110, name=None):
+    """Few query tokens at the end of a long KV set (decode, or a short
+    prefill chunk): query i sits at position S_kv - T + i and holds the
+    DeepSeek-V4-like [window | top-k] row of that position (the window of
+    the <= 128 latest positions, then top-k distinct positions from before
+    the window), -1 padded.  d_v = 512, fp32 sink N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    q, kv, dO, s = _dense(rng, T, S_kv, H, d_qk, 512, True)
+    W = window + topk
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for i in range(T):
+        pos = S_kv - T + i
+        lo = max(0, pos - window + 1)
+        idx[i, : pos - lo + 1] = np.arange(lo, pos + 1, dtype=np.int32)
+        k = min(topk, lo)
+        if k > 0:
+            idx[i, window: window + k] = rng.choice(lo, size=k, replace=False)
+    return Problem(name or f"decode_T{T}_S{S_kv}_H{H}_k{topk}", T, S_kv, H, d_qk, 512, W,
+                   1.0 / math.sqrt(d_qk), q, kv, dO, torch.from_numpy(idx), None, s,
+                   meta=dict(seed=seed, window=window, topk=topk))
+
+
 def make_problem(name: str, **kw) -> Problem:
     return PROBLEMS[name](**kw)
 
@@ -519,6 +541,13 @@ PROBLEMS = {
                                                    name="grid_flash_h64_T2048", **kw),
     "grid_flash_h128_T2048": lambda **kw: make_dsv4(2048, 128, 512, 512, 512, seed=55,
                                                     name="grid_flash_h128_T2048", **kw),
+    # the headline shape at small head counts (the in-kernel head padding of
+    # one 16-head MFMA tile)
+    **{f"dsv4_flash_h{H}": (lambda H: lambda **kw: make_dsv4(4096, H, 576, 512, 512, seed=80 + H,
+                                                             name=f"dsv4_flash_h{H}_T4096", **kw))(H)
+       for H in (1, 8, 24)},
+    # few queries against a 16384-row KV set (window 128 + top-k 1024)
+    **{f"decode_T{T}": (lambda T: lambda **kw: make_decode(T, seed=110 + T, **kw))(T) for T in (1, 16, 64)},
     # the headline with 10 % of its tokens holding a late score spike
     "dsv4_flash_h128_spiky": lambda **kw: make_spiky_dsv4(name="dsv4_flash_h128_T4096_spiky", **kw),
     # the headline's index sets packed to the front with topk_length

@@ -22,12 +22,14 @@ def lib():
 
 def declared_functions():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:smla_status|size_t|const char\*)\s+(smla_\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:smla_status|size_t|int|const char\*)\s+(smla_\w+)\(", src, re.M)))
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["smla_fwd", "smla_bwd_preprocess", "smla_bwd_delta_exact",
+    assert declared_functions() == sorted(["smla_fwd", "smla_fwd_splitkv_workspace_size", "smla_fwd_splitkv",
+                                           "smla_bwd_preprocess", "smla_bwd_delta_exact",
                                            "smla_bwd", "smla_bwd_from_o", "smla_bwd_workspace_size",
+                                           "smla_bwd_chunk_tokens",
                                            "smla_bwd_profiled", "smla_bwd_noalloc", "smla_status_string"])
     from sparse_top_attention_topk_amd import _lib
     assert sorted(_lib.EXPORTED) == declared_functions()
@@ -114,7 +116,19 @@ def _ws_expected(C, S_kv, H, d_qk, W):
     mp = C * W // 64 + min(S_kv, C * W)
     off = a(off + (S_kv + 1) * 4)        # part offsets
     off = a(off + mp * 4)                # part rows
-    return a(off + mp * d_qk * 4)        # part sums
+    off = a(off + mp * d_qk * 4)         # part sums
+    return a(off + C * _bwd_splits(C, W) * H * d_qk * 4)   # dQ shares of split blocks
+
+
+def _bwd_splits(C, W):
+    """Block ranges per token in the backward: none from 256 tokens per chunk
+    on; below, up to about 512 workgroups, at most one range per block."""
+    nb = (W + 63) // 64
+    s = 1 if C >= 256 else min(nb, -(-512 // C))
+    if s < 2:
+        return 0
+    bps = -(-nb // s)
+    return -(-nb // bps)
 
 
 DEFAULT_WS = 8 << 30
@@ -192,3 +206,24 @@ def test_noalloc_rejects_before_touching_the_gpu(lib):
     wide = _dims(lib, W=1 << 23, H=128)
     assert lib.LIB.smla_bwd_noalloc(ctypes.byref(wide), *args) == 7
     assert b"fixed scratch" in lib.LIB.smla_status_string(7)
+
+
+@pytest.mark.parametrize("shape", [
+    (1027, 1027, 64, 576, 192), (300, 300, 64, 576, 192), (128, 256, 128, 576, 1024),
+    (320, 320, 96, 512, 160), (4096, 4096, 128, 576, 640), (64, 16384, 128, 576, 1152),
+])
+def test_chunk_choice_always_fits_its_workspace(shape):
+    """For workspaces from one token's need up to all tokens', the chunk the
+    backward picks has a layout no larger than the workspace given (below
+    256 tokens a smaller chunk can need more, for the dQ shares of split
+    blocks), the chunk is at most T, and all tokens' workspace gives T."""
+    from sparse_top_attention_topk_amd import _lib
+    T, S, H, dqk, W = shape
+    one = _ws_expected(1, S, H, dqk, W)
+    full = _ws_expected(T, S, H, dqk, W)
+    assert _lib.smla_bwd_chunk_tokens(T, S, H, dqk, 512, W, one - 1) == 0
+    assert _lib.smla_bwd_chunk_tokens(T, S, H, dqk, 512, W, full) == T
+    for c in sorted(set([1, 2, 7, 63, 100, 200, 255, 256, 257, 300, T // 3, T - 1]) & set(range(1, T + 1))):
+        for nbytes in (_ws_expected(c, S, H, dqk, W), _ws_expected(c, S, H, dqk, W) + 12345):
+            got = _lib.smla_bwd_chunk_tokens(T, S, H, dqk, 512, W, nbytes)
+            assert 1 <= got <= T and _ws_expected(got, S, H, dqk, W) <= nbytes, (c, nbytes, got)

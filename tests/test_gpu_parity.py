@@ -13,12 +13,20 @@ import torch
 import oracle
 from parity import (compare_full, compare_exact_delta, run_gpu, run_gpu_exact, run_gpu_from_o, run_oracle,
                     oracle_delta_exact, say, check_tensor, check_lse, check_dsink, check_dkv_rows,
-                    referenced_rows, tokens_referencing)
+                    referenced_rows, tokens_referencing, cosine, to_dev)
 from sparse_top_attention_topk_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+
+
+def _dq_close(a, b):
+    """dQ of two runs whose backward split the blocks differently (fewer than
+    256 tokens per chunk): the same fp32 terms summed in other groups, then
+    rounded to bf16, so elements may differ by a bf16 rounding step."""
+    m = np.abs(b).max()
+    return np.abs(a - b).max() <= 2.0 ** -7 * m and cosine(a, b) >= 0.99999
 
 
 def _run_and_compare(p, label):
@@ -218,8 +226,11 @@ def test_blocks_without_valid_slots_change_no_bit(H):
     _run_and_compare(p, f"block-gaps-h{H}")
     a = run_gpu(p, DEV)
     b = run_gpu(wl.pack_live_blocks(p), DEV)
-    for k in ("o", "lse", "dq", "dkv", "delta", "d_sink"):
+    for k in ("o", "lse", "dkv", "delta", "d_sink"):
         assert np.array_equal(a[k], b[k]), f"{k} differs between the gapped and packed rows"
+    # 96 tokens: the backward splits each row's blocks into ranges, and the
+    # live blocks fall into different ranges in the two layouts
+    assert _dq_close(a["dq"], b["dq"]), "dq differs between the gapped and packed rows"
 
 
 def test_nan_prefilled_outputs_fully_written_and_deterministic():
@@ -260,8 +271,14 @@ def test_batched_sequences(compact):
     ds_sum = np.zeros_like(gpu["d_sink"])
     for i, (a, b) in enumerate(p.meta["segments"]):
         g = run_gpu(wl.segment(p, i), DEV)
-        for k in ("o", "lse", "dq", "dkv"):
+        for k in ("o", "lse", "dkv"):
             assert np.array_equal(gpu[k][a:b], g[k]), f"segment {i}: {k} differs"
+        # a sequence of fewer than 256 tokens run alone splits its blocks
+        # (the batch does not): dQ then sums its terms in other groups
+        if b - a >= 256:
+            assert np.array_equal(gpu["dq"][a:b], g["dq"]), f"segment {i}: dq differs"
+        else:
+            assert _dq_close(gpu["dq"][a:b], g["dq"]), f"segment {i}: dq differs"
         ds_sum += g["d_sink"]
     np.testing.assert_allclose(gpu["d_sink"], ds_sum, rtol=1e-5, atol=1e-5)
 
@@ -282,18 +299,21 @@ CHUNK_CASES = {
 def test_chunked_backward(name):
     """A workspace that holds only some tokens makes the backward run chunk by
     chunk (index inversion, S/dP, dQ, dKV partials and reduce per chunk,
-    dKV accumulated over the chunks in token order).  The outputs meet the
-    oracle; O, LSE, Delta, dQ and d_sink are the bits of the one-chunk run,
-    dKV differs from it only by the summation grouping."""
+    dKV accumulated over the chunks in token order; chunks of fewer than 256
+    tokens also split each row's blocks).  The outputs meet the oracle; O,
+    LSE, Delta and d_sink are the bits of the one-chunk run, dKV and dQ differ
+    from it only by the summation grouping."""
     make, C = CHUNK_CASES[name]
     p = make()
     say(f"[gpu] chunked {name}: T={p.T} S_kv={p.S_kv} H={p.H} W={p.W}, workspace of {C} tokens")
     g = run_gpu(p, DEV, ws_tokens=C)
     errors = compare_full(g, run_oracle(p))
     one = run_gpu(p, DEV)
-    for k in ("o", "lse", "delta", "dq", "d_sink"):
+    for k in ("o", "lse", "delta", "d_sink"):
         if g[k] is not None and not np.array_equal(g[k], one[k]):
             errors.append(f"{k} differs from the one-chunk run")
+    if not _dq_close(g["dq"], one["dq"]):
+        errors.append("dq differs from the one-chunk run beyond a bf16 rounding step")
     m = np.abs(one["dkv"]).max()
     e = np.abs(g["dkv"] - one["dkv"]).max()
     say(f"[gpu] chunked {name}: dkv vs one chunk max diff {e:.3e} (max {m:.3e})")
@@ -338,6 +358,55 @@ def test_batched_large_kv_set():
             if not np.array_equal(gpu[k][a:b], g[k]):
                 errors.append(f"segment {i}: {k} differs from the sequence run alone")
     assert not errors, "; ".join(errors)
+
+
+# ---------------------------------------------------------------------------
+# few tokens: the blocks of each row split over several workgroups
+# ---------------------------------------------------------------------------
+SPLIT_CASES = {
+    "decode-T1": lambda: wl.make_problem("decode_T1"),
+    "decode-T16": lambda: wl.make_problem("decode_T16"),
+    "decode-T64": lambda: wl.make_problem("decode_T64"),
+    "decode-T16-h64-d512": lambda: wl.make_decode(16, H=64, d_qk=512, seed=140),
+    "decode-T5-h24-k2048": lambda: wl.make_decode(5, S_kv=8192, H=24, topk=2048, seed=141),
+    "spiky-T128-h96": lambda: wl.make_spiky(96, T=128, frac=0.5),
+    "edge-wide-h128": lambda: wl.make_edge_wide(128),
+}
+
+
+def _fwd_split(p):
+    from sparse_top_attention_topk_amd import _lib
+    d = to_dev(p, DEV)
+    ws_n = _lib.smla_fwd_splitkv_workspace_size(p.T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale)
+    o = torch.full((p.T, p.H, p.d_v), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((p.T, p.H), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = _lib.smla_fwd_splitkv(d["q"], d["kv"], d["idx"], d["length"], d["sink"], p.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    return ws_n, o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(SPLIT_CASES))
+def test_split_kv(name):
+    """Few tokens against long rows: smla_fwd_splitkv runs each token's blocks
+    in up to ceil(W / 64) workgroups and merges them; the backward splits
+    its S/dP, dQ and dKV kernels over block ranges (dQ through fp32
+    partials).  Both meet the oracle element by element; the split forward
+    agrees with smla_fwd to its tolerance."""
+    p = SPLIT_CASES[name]()
+    say(f"[gpu] split kv {name}: T={p.T} S_kv={p.S_kv} H={p.H} d_qk={p.d_qk} W={p.W}")
+    ws_n, o_s, lse_s = _fwd_split(p)
+    assert ws_n > 0, "the case should split"
+    gpu = run_gpu(p, DEV)                    # smla_fwd + the (split) backward
+    ref = run_oracle(p)
+    errors = compare_full(gpu, ref)
+    check_tensor("o (split fwd)", o_s, ref["o"], errors)
+    check_lse(lse_s, ref["lse"], errors)
+    if not np.all(np.isfinite(o_s)):
+        errors.append("split fwd: O not fully written")
+    m = np.abs(gpu["o"]).max()
+    if np.abs(o_s - gpu["o"]).max() > 2.0 ** -7 * m:
+        errors.append(f"split fwd: O differs from smla_fwd by {np.abs(o_s - gpu['o']).max():.3e}")
+    assert not errors, f"{name}: " + "; ".join(errors)
 
 
 # ---------------------------------------------------------------------------

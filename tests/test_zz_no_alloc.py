@@ -3,10 +3,11 @@ against smla_bwd with a workspace of its own: two calls in a row through the
 C ABI, the second on a smaller problem (the scratch keeps the first call's
 contents, which the second must not depend on).
 
-dQ and d_sink do not depend on how the tokens are chunked and must be the
-same bits; dKV sums each row chunk by chunk, so with a chunk size other than
-smla_bwd's it may differ by the summation grouping only (and must be the same
-bits when both run one chunk)."""
+d_sink does not depend on how the tokens are chunked and must be the same
+bits; dKV sums each row chunk by chunk and dQ sums block ranges when a chunk
+has fewer than 256 tokens, so with a chunk size other than smla_bwd's they
+may differ by the summation grouping only (and must be the same bits when
+both run one chunk)."""
 import numpy as np
 import pytest
 import torch
@@ -44,7 +45,13 @@ def _compare(p, label, one_chunk):
     say(f"[gpu] noalloc {label}: T={p.T} S_kv={p.S_kv} H={p.H} W={p.W}")
     _lib.smla_bwd_noalloc(*args, dq=dq1, dkv=dkv1, d_sink=ds1)
     torch.cuda.synchronize()
-    assert torch.equal(dq1, dq0), f"{label}: dq differs from smla_bwd"
+    if one_chunk:
+        assert torch.equal(dq1, dq0), f"{label}: dq differs from smla_bwd"
+    else:
+        md = dq0.float().abs().max().item()
+        ed = (dq1.float() - dq0.float()).abs().max().item()
+        say(f"[gpu] noalloc {label}: dq max diff {ed:.3e} (max {md:.3e})")
+        assert ed <= 2.0 ** -7 * md, f"{label}: dq differs from smla_bwd by {ed:.3e}"
     if ds0 is not None:
         assert torch.equal(ds1, ds0), f"{label}: d_sink differs from smla_bwd"
     assert torch.isfinite(dkv1).all(), f"{label}: dkv not fully written"
