@@ -97,7 +97,7 @@ smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
 
 /* Bytes of device workspace with which smla_fwd_splitkv splits each token's
  * slot blocks over several workgroups: non-zero when the tokens alone (one
- * workgroup per token and group of 64 or 128 heads) give fewer than 256
+ * workgroup per token and group of 64 or 128 heads) give fewer than 128
  * workgroups, i.e. decode and short chunks against long top-k rows; 0 when
  * no split is made (then smla_fwd_splitkv is smla_fwd). */
 size_t smla_fwd_splitkv_workspace_size(const smla_dims* dims);
@@ -181,7 +181,10 @@ int smla_bwd_chunk_tokens(const smla_dims* dims, size_t workspace_bytes);
  * are processed in chunks of equal size, as many tokens per chunk as the
  * workspace holds (all T with smla_bwd_workspace_size bytes unless that is
  * capped); dkv sums a row's contributions chunk by chunk in token order, so
- * its bits depend on the chunk size but not on scheduling.
+ * its bits depend on the chunk size but not on scheduling.  A chunk of fewer
+ * than 128 tokens also splits each row's 64-slot blocks into ranges run by
+ * separate workgroups (so that the GPU is filled); dq is then summed range by
+ * range in fp32, and its bits follow the number of ranges.
  * SMLA_ERR_WORKSPACE if workspace is NULL or holds less than one token's
  * chunk.
  */

@@ -55,19 +55,19 @@ int inversion_subchunks(const smla_dims* d, int C) {
 //   part_off         int32 [S_kv + 1]; part_row int32 [max_parts]
 //   part_sum         fp32 [max_parts, d_qk], max_parts = C * W / 64 + min(S_kv, C * W)
 //                    (a row named n times has ceil(n / 64) parts)
-//   dq_part          fp32 [C, nsplit, H, d_qk] when the blocks are split (C < 256)
+//   dq_part          fp32 [C, nsplit, H, d_qk] when the blocks are split (C < 128)
 struct WsLayout {
     size_t p, ds, chunk, cnt, off, ent, part, poff, prow, psum, dqp, total;
     int max_parts, nsub, nsplit, bps;
 };
 
 // Splits of each token's slot blocks in the backward for chunks of C
-// tokens: one workgroup per token fills the GPU from 256 tokens on; below,
-// the blocks are split until there are about 512 workgroups (at most one
-// split per block).
+// tokens: from 128 tokens on the chunk is run one workgroup per token; below,
+// the blocks are split until one round of about 256 workgroups is filled
+// (at most one split per block).
 void bwd_split_for(const smla_dims* d, int C, int* nsplit, int* bps) {
     const int64_t nb = ((int64_t)d->W + smla::BLK - 1) / smla::BLK;
-    int64_t s = C >= 256 ? 1 : (512 + C - 1) / C;
+    int64_t s = C >= 128 ? 1 : 256 / C;
     if (s > nb) s = nb;
     if (s < 2) {
         *nsplit = 1;
@@ -106,8 +106,10 @@ WsLayout ws_layout(const smla_dims* d, int C) {
 
 // ---- split forward: how many splits over each token's slot blocks.  A
 // token takes one workgroup per head tile; with few tokens the GPU's 256
-// CUs are not filled, so the blocks are split until there are about 512
-// workgroups (at most one split per block).
+// CUs are not filled, so the blocks are split until one round of about 256
+// workgroups (one per CU) is filled, at most one split per block: a second
+// round costs more than the longer ranges, and every split adds its fp32
+// partial O to write and merge.
 struct FwdSplit {
     int nsplit, bps, nb;
 };
@@ -116,8 +118,9 @@ FwdSplit fwd_split_for(const smla_dims* d) {
     const int64_t nb = ((int64_t)d->W + smla::BLK - 1) / smla::BLK;
     const int ht = smla::fwd_head_tile(d->H);
     const int64_t wgs = (int64_t)d->T * ((d->H + ht - 1) / ht);
-    int64_t s = wgs >= 256 ? 1 : (512 + wgs - 1) / wgs;
+    int64_t s = wgs >= 128 ? 1 : 256 / wgs;
     if (s > nb) s = nb;
+    if (s > 64) s = 64;                          // the merge keeps one split per lane
     if (s < 2) return {1, (int)nb, (int)nb};
     const int64_t bps = (nb + s - 1) / s;
     return {(int)((nb + bps - 1) / bps), (int)bps, (int)nb};
@@ -131,9 +134,9 @@ size_t fwd_split_bytes(const smla_dims* d, int nsplit) {
 
 // Largest chunk whose workspace fits in `bytes` (0 if not even one token's
 // does).  Local slot indices (t - t0) * Wp + j and part counts stay in int32.
-// The workspace grows with the chunk from 256 tokens on (no block split);
-// below 256 it also holds the dQ shares of the split blocks, whose size is
-// not monotone in the chunk, so that range is scanned.
+// The workspace grows with the chunk from 128 tokens on (no block split);
+// below 128 it also holds the dQ shares of the split blocks, whose size is
+// not monotone in the chunk, so the range below 256 is scanned.
 int max_chunk(const smla_dims* d, size_t bytes) {
     const int64_t Wp = (int64_t)round_up_blk(d->W);
     int64_t hi = d->T;
@@ -157,7 +160,7 @@ int max_chunk(const smla_dims* d, size_t bytes) {
 
 // Tokens per chunk for a workspace of `bytes`: the largest chunk that fits,
 // evened out over the same number of chunks when the even size fits too (it
-// may not: below 256 tokens a smaller chunk can need more, for the dQ shares
+// may not: below 128 tokens a smaller chunk can need more, for the dQ shares
 // of its split blocks).  0 if not even one token's chunk fits.  The result
 // always satisfies ws_layout(d, C).total <= bytes.
 int chunk_tokens(const smla_dims* d, size_t bytes) {

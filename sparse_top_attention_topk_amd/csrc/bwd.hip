@@ -156,40 +156,66 @@ constexpr int RPART = 64;
 
 __device__ __forceinline__ int nparts(int cnt) { return (cnt + RPART - 1) / RPART; }
 
+// Tiles of 8192 rows: thread i takes rows 8i .. 8i + 7 of the tile (two
+// 16-byte loads, adjacent threads adjacent), the workgroup scans the
+// per-thread sums (within each wave by shuffles, then over the 16 wave
+// sums), and a carry runs from tile to tile.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(1024) void rows_scan_kernel(BwdArgs a) {
-    __shared__ int s_part[1024];
-    __shared__ int s_part2[1024];
+    __shared__ int s_w[2][16];
     const int n = a.S_kv;
-    const int per = (n + 1023) / 1024;
-    const int lo = (int)threadIdx.x * per < n ? (int)threadIdx.x * per : n;
-    const int hi = lo + per < n ? lo + per : n;
-    int sum = 0, sum2 = 0;
-    for (int r = lo; r < hi; ++r) {
-        sum += a.row_cnt[r];
-        sum2 += nparts(a.row_cnt[r]);
-    }
-    s_part[threadIdx.x] = sum;
-    s_part2[threadIdx.x] = sum2;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = (int)threadIdx.x >= d ? s_part[threadIdx.x - d] : 0;
-        const int v2 = (int)threadIdx.x >= d ? s_part2[threadIdx.x - d] : 0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0, carry2 = 0;
+    for (int base = 0; base < n; base += 8192) {
+        const int r0 = base + 8 * tid;
+        int c[8];
+        if (r0 + 8 <= n) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(a.row_cnt + r0);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(a.row_cnt + r0 + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { c[k] = (int)x[k]; c[4 + k] = (int)y[k]; }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = r0 + k < n ? a.row_cnt[r0 + k] : 0;
+        }
+        int sum = 0, sum2 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { sum += c[k]; sum2 += nparts(c[k]); }
+        const int inc = wave_incl_scan(sum, lane), inc2 = wave_incl_scan(sum2, lane);
+        if (lane == 63) { s_w[0][wave] = inc; s_w[1][wave] = inc2; }
         __syncthreads();
-        s_part[threadIdx.x] += v;
-        s_part2[threadIdx.x] += v2;
-        __syncthreads();
+        int wpre = 0, wpre2 = 0, tot = 0, tot2 = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int v = s_w[0][w], v2 = s_w[1][w];
+            if (w < wave) { wpre += v; wpre2 += v2; }
+            tot += v; tot2 += v2;
+        }
+        int run = carry + wpre + inc - sum, run2 = carry2 + wpre2 + inc2 - sum2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (r0 + k < n) {
+                a.row_off[r0 + k] = run;
+                a.part_off[r0 + k] = run2;
+            }
+            run += c[k];
+            run2 += nparts(c[k]);
+        }
+        carry += tot;
+        carry2 += tot2;
+        __syncthreads();                       // s_w is reused by the next tile
     }
-    int run = s_part[threadIdx.x] - sum;     // exclusive prefixes of this thread's rows
-    int run2 = s_part2[threadIdx.x] - sum2;
-    for (int r = lo; r < hi; ++r) {
-        a.row_off[r] = run;
-        a.part_off[r] = run2;
-        run += a.row_cnt[r];
-        run2 += nparts(a.row_cnt[r]);
-    }
-    if (threadIdx.x == 1023) {
-        a.row_off[n] = s_part[1023];
-        a.part_off[n] = s_part2[1023];
+    if (tid == 0) {
+        a.row_off[n] = carry;
+        a.part_off[n] = carry2;
     }
 }
 
@@ -203,8 +229,23 @@ __global__ __launch_bounds__(256) void rows_parts_kernel(BwdArgs a) {
 __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
     extern __shared__ int s_cur[];           // [nr]
     const InvPart P(a);
-    for (int i = threadIdx.x; i < P.nr; i += 256)
-        s_cur[i] = a.row_off[P.r0 + i] + a.chunk_cnt[(size_t)blockIdx.x * a.S_kv + P.r0 + i];
+    {
+        const int* ro = a.row_off + P.r0;
+        const int* cc = a.chunk_cnt + (size_t)blockIdx.x * a.S_kv + P.r0;
+        for (int i0 = 0; i0 < P.nr; i0 += 8 * 256) {
+            int v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * 256 + (int)threadIdx.x;
+                v[k] = i < P.nr ? ro[i] + cc[i] : 0;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * 256 + (int)threadIdx.x;
+                if (i < P.nr) s_cur[i] = v[k];
+            }
+        }
+    }
     __syncthreads();
     for (int t = P.t_begin; t < P.t_end; ++t) {
         const int L = row_length(a.len, t, a.W);
@@ -726,10 +767,19 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63;
     if (row >= a.Tc * a.H) return;
     const int tl = row / a.H, h = row - tl * a.H;
+    const float* src = a.dq_part + ((size_t)tl * a.nsplit * a.H + h) * DQK;    // split s: + s * H * DQK
+    const size_t sstride = (size_t)a.H * DQK;
     for (int c = 4 * lane; c < DQK; c += 256) {
         f32x4 acc = zero4();
-        for (int s = 0; s < a.nsplit; ++s)
-            acc += *reinterpret_cast<const f32x4*>(a.dq_part + (((size_t)tl * a.nsplit + s) * a.H + h) * DQK + c);
+        int s = 0;
+        for (; s + 4 <= a.nsplit; s += 4) {          // four shares in flight, summed in split order
+            f32x4 x[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[k] = *reinterpret_cast<const f32x4*>(src + (s + k) * sstride + c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc += x[k];
+        }
+        for (; s < a.nsplit; ++s) acc += *reinterpret_cast<const f32x4*>(src + s * sstride + c);
         st4(a.dq + ((size_t)(a.t0 + tl) * a.H + h) * DQK + c, cvt4(acc[0], acc[1], acc[2], acc[3]));
     }
 }

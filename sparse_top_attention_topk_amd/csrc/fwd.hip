@@ -443,6 +443,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 //   O = sum_s f_s O_s / sum_s f_s lr_s,   LSE = (M + log2 sum_s f_s l_s) ln 2,
 // the same normalisation (by the rounded weights) and LSE as one workgroup
 // over all blocks; then the sink fold of the forward's epilogue.
+// (nsplit <= 64: lane s holds split s's sums)
 __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
     constexpr int DV = 512;
     const int row = (int)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -450,24 +451,37 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
     if (row >= a.T * a.H) return;
     const int t = row / a.H, h = row - t * a.H;
     const size_t base = (size_t)t * a.nsplit * a.H + h;       // split s: base + s * H
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) {
-        const f32x4 st = *reinterpret_cast<const f32x4*>(a.spart + (base + (size_t)s * a.H) * 4);
-        if (st[1] > 0.f) M = fmaxf(M, st[0]);
-    }
+    // lane s < nsplit holds split s's stats; M over the splits with a valid slot
+    f32x4 st = zero4();
+    if (lane < a.nsplit) st = *reinterpret_cast<const f32x4*>(a.spart + (base + (size_t)lane * a.H) * 4);
+    float M = st[1] > 0.f ? st[0] : -INFINITY;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    // lane s: its split's factor 2^(m_s - M) (0 without a valid slot)
+    const float fs = (M != -INFINITY && st[1] > 0.f) ? exp2f(st[0] - M) : 0.f;
     f32x4 acc0 = zero4(), acc1 = zero4();
     float l = 0.f, lr = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < a.nsplit; ++s) {
-            const size_t r = base + (size_t)s * a.H;
-            const f32x4 st = *reinterpret_cast<const f32x4*>(a.spart + r * 4);
-            if (!(st[1] > 0.f)) continue;
-            const float f = exp2f(st[0] - M);
-            l += f * st[1];
-            lr += f * st[2];
-            const float* op = a.opart + r * DV + 8 * lane;
-            acc0 += f * *reinterpret_cast<const f32x4*>(op);
-            acc1 += f * *reinterpret_cast<const f32x4*>(op + 4);
+        // four splits' rows in flight, summed in split order
+        for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
+            f32x4 x[4][2];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int s = s0 + k < a.nsplit ? s0 + k : a.nsplit - 1;
+                const float* op = a.opart + (base + (size_t)s * a.H) * DV + 8 * lane;
+                x[k][0] = *reinterpret_cast<const f32x4*>(op);
+                x[k][1] = *reinterpret_cast<const f32x4*>(op + 4);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (s0 + k >= a.nsplit) break;
+                const float f = __shfl(fs, s0 + k, 64);
+                const float sl = __shfl(st[1], s0 + k, 64), slr = __shfl(st[2], s0 + k, 64);
+                l += f * sl;
+                lr += f * slr;
+                acc0 += f * x[k][0];
+                acc1 += f * x[k][1];
+            }
         }
     }
     const bool nonempty = l > 0.f;

@@ -121,10 +121,10 @@ def _ws_expected(C, S_kv, H, d_qk, W):
 
 
 def _bwd_splits(C, W):
-    """Block ranges per token in the backward: none from 256 tokens per chunk
-    on; below, up to about 512 workgroups, at most one range per block."""
+    """Block ranges per token in the backward: none from 128 tokens per chunk
+    on; below, up to about 256 workgroups, at most one range per block."""
     nb = (W + 63) // 64
-    s = 1 if C >= 256 else min(nb, -(-512 // C))
+    s = 1 if C >= 128 else min(nb, 256 // C)
     if s < 2:
         return 0
     bps = -(-nb // s)
@@ -215,7 +215,7 @@ def test_noalloc_rejects_before_touching_the_gpu(lib):
 def test_chunk_choice_always_fits_its_workspace(shape):
     """For workspaces from one token's need up to all tokens', the chunk the
     backward picks has a layout no larger than the workspace given (below
-    256 tokens a smaller chunk can need more, for the dQ shares of split
+    128 tokens a smaller chunk can need more, for the dQ shares of split
     blocks), the chunk is at most T, and all tokens' workspace gives T."""
     from sparse_top_attention_topk_amd import _lib
     T, S, H, dqk, W = shape
@@ -227,3 +227,22 @@ def test_chunk_choice_always_fits_its_workspace(shape):
         for nbytes in (_ws_expected(c, S, H, dqk, W), _ws_expected(c, S, H, dqk, W) + 12345):
             got = _lib.smla_bwd_chunk_tokens(T, S, H, dqk, 512, W, nbytes)
             assert 1 <= got <= T and _ws_expected(got, S, H, dqk, W) <= nbytes, (c, nbytes, got)
+
+
+def test_forward_split_count():
+    """The split forward splits only when the tokens give fewer than 128
+    workgroups, fills about one round of 256, never exceeds one split per
+    block nor 64 splits (the merge keeps one per lane)."""
+    from sparse_top_attention_topk_amd import _lib
+    for T, H, W, want in [(4096, 128, 640, 0), (128, 128, 1152, 0), (1, 128, 1152, 18), (64, 128, 1152, 4),
+                          (16, 128, 1152, 16), (1, 8, 64, 0), (1, 128, 1 << 16, 64), (5, 24, 2176, 34)]:
+        nb = -(-W // 64)
+        ws = _lib.smla_fwd_splitkv_workspace_size(T, 16384, H, 576, 512, W)
+        if want == 0:
+            assert ws == 0, (T, H, W)
+            continue
+        bps = -(-nb // want)
+        ns = -(-nb // bps)
+        a = lambda x: (x + 255) // 256 * 256
+        rows = T * ns * H
+        assert ws == a(rows * 512 * 4) + a(rows * 16), (T, H, W, ws)

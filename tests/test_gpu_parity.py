@@ -23,7 +23,7 @@ DEV = torch.device("cuda:0")
 
 def _dq_close(a, b):
     """dQ of two runs whose backward split the blocks differently (fewer than
-    256 tokens per chunk): the same fp32 terms summed in other groups, then
+    128 tokens per chunk): the same fp32 terms summed in other groups, then
     rounded to bf16, so elements may differ by a bf16 rounding step."""
     m = np.abs(b).max()
     return np.abs(a - b).max() <= 2.0 ** -7 * m and cosine(a, b) >= 0.99999
@@ -273,9 +273,9 @@ def test_batched_sequences(compact):
         g = run_gpu(wl.segment(p, i), DEV)
         for k in ("o", "lse", "dkv"):
             assert np.array_equal(gpu[k][a:b], g[k]), f"segment {i}: {k} differs"
-        # a sequence of fewer than 256 tokens run alone splits its blocks
+        # a sequence of fewer than 128 tokens run alone splits its blocks
         # (the batch does not): dQ then sums its terms in other groups
-        if b - a >= 256:
+        if b - a >= 128:
             assert np.array_equal(gpu["dq"][a:b], g["dq"]), f"segment {i}: dq differs"
         else:
             assert _dq_close(gpu["dq"][a:b], g["dq"]), f"segment {i}: dq differs"
@@ -299,7 +299,7 @@ CHUNK_CASES = {
 def test_chunked_backward(name):
     """A workspace that holds only some tokens makes the backward run chunk by
     chunk (index inversion, S/dP, dQ, dKV partials and reduce per chunk,
-    dKV accumulated over the chunks in token order; chunks of fewer than 256
+    dKV accumulated over the chunks in token order; chunks of fewer than 128
     tokens also split each row's blocks).  The outputs meet the oracle; O,
     LSE, Delta and d_sink are the bits of the one-chunk run, dKV and dQ differ
     from it only by the summation grouping."""
@@ -369,8 +369,9 @@ SPLIT_CASES = {
     "decode-T64": lambda: wl.make_problem("decode_T64"),
     "decode-T16-h64-d512": lambda: wl.make_decode(16, H=64, d_qk=512, seed=140),
     "decode-T5-h24-k2048": lambda: wl.make_decode(5, S_kv=8192, H=24, topk=2048, seed=141),
-    "spiky-T128-h96": lambda: wl.make_spiky(96, T=128, frac=0.5),
-    "edge-wide-h128": lambda: wl.make_edge_wide(128),
+    "spiky-T96-h96": lambda: wl.make_spiky(96, T=96, window=32, topk=160, frac=0.5),
+    "decode-T1-k8064": lambda: wl.make_decode(1, H=128, topk=8064, seed=142),   # 128 blocks: 64 splits
+    "edge-wide-h128-T64": lambda: wl.make_edge_wide(128, T=64),
 }
 
 
@@ -459,7 +460,7 @@ FROM_O_CASES = {
     "tiny-sink": lambda: wl.make_tiny(seed=0, sink=True, compact=False),
     "tiny-compact": lambda: wl.make_tiny(seed=0, sink=True, compact=True),
     "edge-compact-h24": lambda: wl.make_edge_compact(24),
-    "edge-wide-h128": lambda: wl.make_edge_wide(128),
+    "edge-wide-h128-T64": lambda: wl.make_edge_wide(128, T=64),
     "edge-sink-h64": lambda: wl.make_edge_sink(64),
     "width-118-h128": lambda: wl.make_edge_width118(128),
     "batched": lambda: wl.make_batched(),

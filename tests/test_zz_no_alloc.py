@@ -5,7 +5,7 @@ contents, which the second must not depend on).
 
 d_sink does not depend on how the tokens are chunked and must be the same
 bits; dKV sums each row chunk by chunk and dQ sums block ranges when a chunk
-has fewer than 256 tokens, so with a chunk size other than smla_bwd's they
+has fewer than 128 tokens, so with a chunk size other than smla_bwd's they
 may differ by the summation grouping only (and must be the same bits when
 both run one chunk)."""
 import numpy as np
