@@ -382,7 +382,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         // partials of this split: the unnormalised O^T (lane (g, n) holds
         // columns 16 mc + 4g .. +3 of head n), and per head the reference
         // max (log2 domain; -inf without a valid slot), the fp32 sum of the
-        // weights and the sum of their bf16 roundings
+        // weights and the sum of their bf16 roundings.  Lane indices from an
+        // opaque copy of the lane, as in the epilogue below.
+        int lane_s;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(lane_s) : "v"(lane));
+        const int g = lane_s >> 4, n = lane_s & 15;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int head = h_wave + nt * 16 + n;
@@ -401,11 +405,17 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         return;
     }
 
-    // epilogue: normalise, fold the sink, stage O^T through LDS as O rows
+    // epilogue: normalise, fold the sink, stage O^T through LDS as O rows.
+    // The lane's indices are derived again from an opaque copy of the lane,
+    // so that no epilogue address is computed ahead and kept live (and
+    // spilled) across the block loop.
+    int lane_e;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_e) : "v"(lane));
+    const int g_e = lane_e >> 4, n_e = lane_e & 15;
     float lse_v[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int head = h_wave + nt * 16 + n;
+        const int head = h_wave + nt * 16 + n_e;
         float l = l_run[nt], lr = l_rnd[nt];
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
@@ -416,15 +426,15 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         float f = (nonempty && lr > 0.f) ? 1.0f / lr : 0.f;
         if (a.sink != nullptr && nonempty && head < a.H) f *= sigmoid(lse_v[nt] - a.sink[head]);
         // staging row hr holds O[head] with 16-byte chunk c at c ^ (hr % 16)
-        const int hr = wave * NT * 16 + nt * 16 + n;
+        const int hr = wave * NT * 16 + nt * 16 + n_e;
         __bf16* sp = hr < 64 ? s_tile0 + hr * C::DV : s_tile1 + (hr - 64) * C::DV;
 #pragma unroll
         for (int mc = 0; mc < C::MC; ++mc) {
             const f32x4 v = oacc[mc][nt] * f;
-            const int col = (mc * 16 + 4 * g) ^ ((hr & 15) << 3);
+            const int col = (mc * 16 + 4 * g_e) ^ ((hr & 15) << 3);
             st4(sp + col, cvt4(v[0], v[1], v[2], v[3]));
         }
-        if (active && g == 0 && head < a.H) a.lse[(size_t)t * a.H + head] = lse_v[nt];
+        if (active && g_e == 0 && head < a.H) a.lse[(size_t)t * a.H + head] = lse_v[nt];
     }
     __syncthreads();
     // coalesced stores: HT rows of DV bf16, 16 bytes per thread per step
