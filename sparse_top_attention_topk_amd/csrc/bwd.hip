@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const __bf16* __restric
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const size_t off = (size_t)row * 512 + lane * 8;
-    const bf16x8 x = ld8(o + off), y = ld8(dO + off);
+    const bf16x8 x = ld8_nt(o + off), y = ld8_nt(dO + off);
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc += (float)x[j] * (float)y[j];

@@ -45,6 +45,17 @@ __device__ __forceinline__ bf16x8 ld8(const __bf16* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Streaming (non-temporal) loads, for the Delta pass, which reads O and dO
+// once and nothing else: -11 % at the headline.  Measured elsewhere they cost
+// time or only moved it: the gather kernels' q, dO and dS loads (+1 to +28 %),
+// the reduce's partial rows (+11 %: some are still cached from the dKV
+// kernel), the dKV kernel's staging of q, dO, P and dS (-3 % there, +7 % in
+// the reduce after it); streaming stores of 8-byte pieces were up to 2.6x
+// slower (not combined into whole lines).
+__device__ __forceinline__ bf16x8 ld8_nt(const __bf16* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
 __device__ __forceinline__ bf16x8 lds8(const __bf16* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -70,6 +81,7 @@ __device__ __forceinline__ bf16x8 cvt8(f32x4 lo, f32x4 hi) {
 __device__ __forceinline__ void st4(__bf16* p, bf16x4 v) {
     *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
 }
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
