@@ -508,6 +508,51 @@ def make_decode(T, S_kv=16384, H=128, d_qk=576, topk=1024, window=128, seed=110,
                    meta=dict(seed=seed, window=window, topk=topk))
 
 
+def make_random(seed):
+    """A small problem with every size and index property drawn at random
+    (seeded): T in [1, 300], S_kv in [1, 2000], H in [1, 128], d_qk 512 or
+    576, W in [1, 1500], compact or non-compact layout, no sink, a finite
+    sink or saturating ones, rows whose valid slots sit anywhere among -1,
+    indices >= S_kv and below -1, some rows empty and some with duplicate
+    indices.  meta["ws_tokens"]: a workspace size (in tokens) to run the
+    backward with, sometimes smaller than T (token chunks)."""
+    rng = np.random.default_rng(10_000 + seed)
+    T = int(rng.integers(1, 301))
+    S = int(rng.integers(1, 2001))
+    H = int(rng.choice([1, 2, 7, 16, 23, 32, 33, 48, 64, 65, 80, 96, 100, 127, 128]))
+    dqk = int(rng.choice([512, 576]))
+    W = int(rng.integers(1, 1501))
+    compact = bool(rng.random() < 0.4)
+    sink_kind = rng.choice(["none", "finite", "finite", "saturating"])
+    q, kv, dO, _ = _dense(rng, T, S, H, dqk, 512, False)
+    sink = None
+    if sink_kind == "finite":
+        sink = torch.from_numpy(rng.standard_normal(size=(H,), dtype=np.float32))
+    elif sink_kind == "saturating":
+        sink = torch.tensor([SATURATING_SINKS[h % 4] if h % 3 == 0 else float(rng.standard_normal())
+                             for h in range(H)], dtype=torch.float32)
+    idx = np.full((T, W), -1, dtype=np.int32)
+    length = np.zeros(T, dtype=np.int32) if compact else None
+    for t in range(T):
+        if rng.random() < 0.05:
+            continue                                   # empty row
+        n = int(rng.integers(1, min(W, S) + 1))
+        rows = rng.choice(S, size=n, replace=bool(rng.random() < 0.1)).astype(np.int32)
+        if compact:
+            length[t] = n + int(rng.integers(0, 3)) if rng.random() < 0.1 else n
+            idx[t, :n] = rows
+            idx[t, n:] = rng.integers(-5, S + 5, size=W - n)   # tail: ignored by position
+        else:
+            pos = rng.choice(W, size=n, replace=False)
+            idx[t, pos] = rows
+            bad = rng.random(W) < 0.03                 # out-of-range values among the padding
+            idx[t, bad & (idx[t] < 0)] = rng.integers(S, S + 100, size=int((bad & (idx[t] < 0)).sum()))
+    ws_tokens = T if rng.random() < 0.7 else int(rng.integers(1, T + 1))
+    return Problem(f"random_{seed}", T, S, H, dqk, 512, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), None if length is None else torch.from_numpy(length), sink,
+                   meta=dict(seed=seed, ws_tokens=ws_tokens, sink_kind=str(sink_kind)))
+
+
 def make_problem(name: str, **kw) -> Problem:
     return PROBLEMS[name](**kw)
 
