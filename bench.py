@@ -285,8 +285,8 @@ def main():
 
 # kernel-name fragment of each timed stage (for the counter profile)
 STAGE_KERNEL = {"fwd": ("fwd_kernel",), "preprocess": ("preprocess_kernel",),
-                "index_inversion": ("rows_",), "sdp": ("bwd_sdp_kernel",),
-                "dq": ("bwd_dq_kernel",), "dkv": ("bwd_dkv_kernel",),
+                "index_inversion": ("rows_",), "sdp_dq": ("bwd_sdq_kernel",),
+                "dq_merge": ("dq_reduce_kernel",), "dkv": ("bwd_dkv_kernel",),
                 "dkv_reduce": ("dkv_part_kernel", "dkv_combine_kernel"),
                 "dsink": ("dsink_kernel",), "delta_exact": ("delta_exact_kernel",)}
 
@@ -307,8 +307,7 @@ def stage_work(p, n):
         "fwd": (2.0 * H * (dqk + dv) * n, gath + qb + ob + T * W * 4 + T * H * 4),
         "preprocess": (0.0, 2 * ob + T * H * 4),
         "index_inversion": (0.0, T * W * 4),
-        "sdp": (2.0 * H * (dqk + dv) * n, gath + qb + ob),
-        "dq": (2.0 * H * dqk * n, gath + qb),
+        "sdp_dq": (2.0 * H * (dqk + dv) * n + 2.0 * H * dqk * n, gath + 2 * qb + ob),
         "dkv": (2.0 * H * (dqk + dv) * n, qb + ob),
         "dkv_reduce": (0.0, S * dqk * 4),
         "dsink": (0.0, 2 * T * H * 4),

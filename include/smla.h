@@ -211,8 +211,10 @@ smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv
                             const float* attn_sink, void* dq, float* dkv, float* d_sink,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of stages smla_bwd runs, in order: index inversion, S/P/dP/dS,
- * dQ, per-slot dKV contributions, dKV row reduce, d_sink. */
+/* Number of stages smla_bwd runs, in order: index inversion, S/P/dP/dS with
+ * dQ (one pass), the merge of dQ shares when a token's blocks are split over
+ * several workgroups (empty otherwise), per-slot dKV contributions, dKV row
+ * reduce, d_sink. */
 #define SMLA_BWD_STAGES 6
 
 /* smla_bwd with stage timing, for benchmarks and profilers.  Computes exactly

@@ -73,7 +73,7 @@ EXPORTED = ("smla_fwd", "smla_fwd_splitkv_workspace_size", "smla_fwd_splitkv", "
 
 SMLA_NOALLOC_SCRATCH_BYTES = 256 << 20
 
-BWD_STAGES = ("index_inversion", "sdp", "dq", "dkv", "dkv_reduce", "dsink")
+BWD_STAGES = ("index_inversion", "sdp_dq", "dq_merge", "dkv", "dkv_reduce", "dsink")
 
 
 def _check(status: int, what: str):

@@ -15,11 +15,13 @@
 //                invert the index lists: every valid (token, slot) is listed
 //                under its KV row, in token order (row r owns the segment
 //                [off[r], off[r+1]) of the list)
-//   bwd_sdp      one workgroup per token, all heads: gathers each 64-slot KV
-//                tile (async, double-buffered), recomputes S, P, dP, dS with
-//                bf16 MFMA and stores P and scale*dS (bf16) to the workspace
-//   bwd_dq       one workgroup per token: gathers the KV tiles again and
-//                accumulates dQ^T = K^T (scale dS)^T in registers
+//   bwd_sdq      one workgroup per token and 64 heads: gathers each 64-slot
+//                KV tile (async, double-buffered), recomputes S, P, dP, dS
+//                with bf16 MFMA, stores P and scale*dS (bf16) to the workspace
+//                and accumulates dQ^T = K^T (scale dS)^T in registers from the
+//                same tile and the dS still in registers
+//   dq_reduce    (block ranges split over several workgroups only) sums the
+//                ranges' fp32 dQ shares in order
 //   bwd_dkv      one workgroup per token: contracts over all heads,
 //                u = (scale dS)^T q + P^T dO per valid slot (fp32 accumulate),
 //                written to the slot's row of a [T * Wp] partial buffer in
@@ -36,9 +38,10 @@
 //   dsink        one workgroup per head: sum over tokens in token order
 // No fp32 atomics touch dkv: the scatter is a write of per-slot partials plus
 // a streaming reduce.  A 64-slot block without a valid slot (the tail of a
-// non-compact row) runs no math in bwd_sdp, bwd_dq and bwd_dkv, and its P and
-// dS are never stored or read: it would add exact zeros.  An empty row (no valid slot) is a uniform branch: dQ = 0
-// is written and the token's q, dO, lse and delta are not read.
+// non-compact row) runs no math in bwd_sdq and bwd_dkv, and its P and dS are
+// never stored or read: it would add exact zeros.  An empty row (no valid
+// slot) is a uniform branch: dQ = 0 is written and the token's q, dO, lse and
+// delta are not read.
 #include "kv_tile.h"
 #include "launch.h"
 
@@ -304,7 +307,10 @@ struct GatherSpread {
 };
 
 // post() runs once, right after the first block's gather is issued: work that
-// waits for its own loads there overlaps them with that gather.
+// waits for its own loads there overlaps them with that gather.  early() runs
+// once, right after the loads of the row's first indices are issued and
+// before they are waited for: loads it issues travel with them (they complete
+// in issue order, so the wait for the indices does not wait for them).
 struct NoPost {
     __device__ void operator()() const {}
 };
@@ -322,11 +328,11 @@ __device__ __forceinline__ BlockRange block_range(const BwdArgs& a, int L) {
     return {b_lo, L < j_end ? L : j_end};
 }
 
-template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost>
+template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost, typename Early = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
                                                 int (*s_rows)[BLK], int* s_live, int* s_last, int t, int L, int nblk,
                                                 BlockRange rg, int wave, int lane, Body&& body, Pre&& pre = Pre{},
-                                                Post&& post = Post{}) {
+                                                Post&& post = Post{}, Early&& early = Early{}) {
     const int b_lo = rg.b_lo, j_hi = rg.j_hi;
     using Tile = KvTileSwz<DQK>;
     using P0 = std::integral_constant<int, 0>;
@@ -334,29 +340,45 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
     // The row's last valid slot: the blocks after its block hold padding only
-    // (the tail of a non-compact row) and are not run.  Its loads go out with
-    // those of the first slot rows.
+    // (the tail of a non-compact row) and are not run.  The raw indices of the
+    // range's first 4 x NW x 64 slots (which hold the first two blocks: the
+    // slot rows of block b_lo are v[0] of threads 0..63) and of block
+    // b_lo + 1 go out in one batch, then early()'s loads behind them.
     {
         constexpr int NTH = NW * 64;
-        int last = -1;
-        for (int j0 = b_lo * BLK; j0 < j_hi; j0 += 4 * NTH) {
-            int v[4];
+        static_assert(NTH >= 2 * BLK, "the first index batch must cover two blocks");
+        const int j_first = b_lo * BLK;
+        int v[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = raw_index_b(a, t, j0 + k * NTH + tid);
+        for (int k = 0; k < 4; ++k) v[k] = raw_index_b(a, t, j_first + k * NTH + tid);
+        const int r1 = raw_index_b(a, t, j_first + BLK + (tid & (BLK - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+        early();
+        __builtin_amdgcn_sched_barrier(0);
+        int last = -1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = j_first + k * NTH + tid;
+            if (valid_row_b(v[k], j, j_hi, a.S_kv) >= 0) last = j;
+        }
+        for (int j0 = j_first + 4 * NTH; j0 < j_hi; j0 += 4 * NTH) {     // rows longer than one batch
+            int u[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) u[k] = raw_index_b(a, t, j0 + k * NTH + tid);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int j = j0 + k * NTH + tid;
-                if (valid_row_b(v[k], j, j_hi, a.S_kv) >= 0) last = j;
+                if (valid_row_b(u[k], j, j_hi, a.S_kv) >= 0) last = j;
             }
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m, 64));
         if (lane == 0) s_last[wave] = last;
-    }
-    if (tid < BLK) {
-        put_rows(s_rows[0], &s_live[0], slot_row(a.idx, t, a.W, j_hi, a.S_kv, b_lo * BLK + tid), tid);
-        put_rows(s_rows[1], &s_live[1], slot_row(a.idx, t, a.W, j_hi, a.S_kv, (b_lo + 1) * BLK + tid), tid);
-        put_rows(s_rows[2], &s_live[2], -1, tid);        // written again before any block reads it
+        if (tid < BLK) {
+            put_rows(s_rows[0], &s_live[0], valid_row_b(v[0], j_first + tid, j_hi, a.S_kv), tid);
+            put_rows(s_rows[1], &s_live[1], valid_row_b(r1, j_first + BLK + tid, j_hi, a.S_kv), tid);
+            put_rows(s_rows[2], &s_live[2], -1, tid);    // written again before any block reads it
+        }
     }
     __syncthreads();
     int last = s_last[0];
@@ -406,21 +428,21 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
 }
 
 // ---------------------------------------------------------------------------
-// bwd_sdp: S, P, dP, dS for all heads of one token (NW waves x NT x 16 heads).
-// q and dO stay in registers as the B operands of S^T = K Q^T and
-// dP^T = V dO^T.  Per 64-slot block, two halves of 32 slots.
+// delta_exact: Delta = sum_j P_j dP_j per head over the token's valid slots,
+// fp32, from the same S^T = K Q^T and dP^T = V dO^T as the backward (NW waves
+// x NT x 16 heads).  q and dO stay in registers as the B operands.  Per
+// 64-slot block, two halves of 32 slots.
 // ---------------------------------------------------------------------------
-template <int DQK, int NW, int NT, bool EXACT>
-__device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
-                                          const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
-                                          const bf16x8 (&qop)[NT][DQK / 32],
-                                          const bf16x8 (&dop)[NT][16], const float (&lse2)[NT],
-                                          const float (&dlt)[NT], float (&pdp)[NT], int t, int h_wave,
-                                          int b, int lane, const GatherSpread<DQK, NW>& gs) {
+template <int DQK, int NW, int NT>
+__device__ __forceinline__ void delta_exact_block(const BwdArgs& a, const __bf16* tile,
+                                                  const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
+                                                  const bf16x8 (&qop)[NT][DQK / 32],
+                                                  const bf16x8 (&dop)[NT][16], const float (&lse2)[NT],
+                                                  float (&pdp)[NT], int lane, const GatherSpread<DQK, NW>& gs) {
     using Tile = KvTileSwz<DQK>;
     constexpr int KS = DQK / 32, KV_ = 16;
     static_assert(GatherSpread<DQK, NW>::STEPS <= KS, "the gather must fit in the first half's S loop");
-    const int g = lane >> 4, n = lane & 15;
+    const int g = lane >> 4;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         f32x4 sacc[2][NT], dpacc[2][NT];
@@ -450,49 +472,22 @@ __device__ __forceinline__ void sdp_block(const BwdArgs& a, const __bf16* tile,
             if (half == 0) gs.step(ks);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (EXACT) {
-            // Delta = sum_j P_j dP_j over the token's valid slots, fp32
+        // P = 2^(s * scale * log2 e - LSE_tot * log2 e), masked; sum P dP
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
-                        const float p = ok ? fast_exp2(sacc[m][nt][i] * a.scale_log2 - lse2[nt]) : 0.f;
-                        pdp[nt] = __builtin_fmaf(p, dpacc[m][nt][i], pdp[nt]);
-                    }
-            continue;
-        }
-        // P = 2^(s * scale * log2 e - LSE_tot * log2 e), masked; dS' = scale P (dP - Delta)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int head = h_wave + nt * 16 + n;
-            f32x4 pv[2], dsv[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool ok = rows[(2 * half + m) * 16 + 4 * g + i] >= 0;
                     const float p = ok ? fast_exp2(sacc[m][nt][i] * a.scale_log2 - lse2[nt]) : 0.f;
-                    pv[m][i] = p;
-                    dsv[m][i] = p * (dpacc[m][nt][i] - dlt[nt]) * a.scale;
+                    pdp[nt] = __builtin_fmaf(p, dpacc[m][nt][i], pdp[nt]);
                 }
-            }
-            if (head < a.H) {
-                const size_t base = ((size_t)(t - a.t0) * a.H + head) * a.Wp + b * BLK + half * 32 + 4 * g;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    st4(a.ws_p + base + m * 16, cvt4(pv[m][0], pv[m][1], pv[m][2], pv[m][3]));
-                    st4(a.ws_ds + base + m * 16, cvt4(dsv[m][0], dsv[m][1], dsv[m][2], dsv[m][3]));
-                }
-            }
-        }
     }
 }
 
 // Delta = sum over the d_v columns of O dO in fp32 (the preprocess pass's
-// arithmetic, fused into the S/dP kernel): lane (g, n) takes columns
+// arithmetic, fused into the backward's S/dP pass): lane (g, n) takes columns
 // 32 ks + 8g .. +7 of head h_wave + 16 nt + n (the layout of the dO operands,
 // which dO_at(nt, ks, row) returns), then the four lane groups are summed.
 // Writes delta_out for the existing heads and returns the sums in dlt.
@@ -520,10 +515,8 @@ __device__ __forceinline__ void fused_delta(const BwdArgs& a, int t, int h_wave,
     }
 }
 
-// One token of bwd_sdp (EXACT = false) or of the exact-Delta pass (EXACT =
-// true: the same S and dP, summed as P dP per head instead of stored).
-template <int DQK, int NW, int NT, bool EXACT>
-__device__ __forceinline__ void sdp_token(const BwdArgs& a) {
+template <int DQK, int NW, int NT>
+__global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
     using Tile = KvTileSwz<DQK>;
     constexpr int KS = DQK / 32, HT = NW * NT * 16;
     __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
@@ -536,34 +529,25 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the longest rows first
     const int h_wave = (int)blockIdx.y * HT + wave * NT * 16;
     const bool active = h_wave < a.H;
     const int L = row_length(a.len, t, a.W);
     const int nblk = (L + BLK - 1) / BLK;
-    if (nblk == 0) {                             // uniform: nothing to store
-        if (EXACT && g == 0)                     // (Delta of an empty row: 0)
+    if (nblk == 0) {                             // uniform: Delta of an empty row is 0
+        if (g == 0)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int head = h_wave + nt * 16 + n;
                 if (head < a.H) a.delta_out[(size_t)t * a.H + head] = 0.f;
             }
-        if (!EXACT && a.o != nullptr) {          // O dO still, as the preprocess pass would
-            float unused[NT];
-            fused_delta<NT>(a, t, h_wave, lane,
-                            [&](int, int ks, size_t row) { return ld8(a.dO + row * 512 + 32 * ks + 8 * g); },
-                            unused);
-        }
         return;
     }
 
-    // q, dO (and the LSE, Delta scalars) go to registers once the first
-    // tile's gather is in flight.  With o given, Delta = sum O dO is formed
-    // from dO before q is loaded (dO, O and q at once would not fit the
-    // registers): one more round trip than loading q and dO together, which
-    // costs about what the separate preprocess pass does.
+    // q, dO and the LSE go to registers once the first tile's gather is in
+    // flight
     bf16x8 qop[NT][KS], dop[NT][16];
-    float lse2[NT], dlt[NT];
+    float lse2[NT];
     auto post = [&]() {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -573,21 +557,11 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
 #pragma unroll
             for (int ks = 0; ks < 16; ++ks) dop[nt][ks] = hv ? ld8(a.dO + row * 512 + 32 * ks + 8 * g) : zero8();
             lse2[nt] = 0.f;
-            dlt[nt] = 0.f;
             if (hv) {
                 const float l = a.lse[row];
                 const float lt = a.sink ? glae(l, a.sink[head]) : l;
                 lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
-                if (!EXACT && a.o == nullptr) dlt[nt] = a.delta[row];
             }
-        }
-        if (!EXACT && a.o != nullptr)            // uniform
-            fused_delta<NT>(a, t, h_wave, lane, [&](int nt, int ks, size_t) { return dop[nt][ks]; }, dlt);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int head = h_wave + nt * 16 + n;
-            const bool hv = head < a.H;
-            const size_t row = (size_t)t * a.H + (hv ? head : 0);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = hv ? ld8(a.q + row * DQK + 32 * ks + 8 * g) : zero8();
         }
@@ -598,164 +572,21 @@ __device__ __forceinline__ void sdp_token(const BwdArgs& a) {
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
                              wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
+                             [&](const __bf16* tile, const int* rows, int, auto, const auto& gs, bool live) {
                                  if (active && live)
-                                     sdp_block<DQK, NW, NT, EXACT>(a, tile, TL, rows, qop, dop, lse2, dlt,
-                                                                   pdp, t, h_wave, b, lane, gs);
+                                     delta_exact_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, pdp, lane,
+                                                                    gs);
                                  else
                                      gs.all();
                              }, NoPre{}, post);
-    if constexpr (EXACT) {
-        // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            float v = pdp[nt];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            const int head = h_wave + nt * 16 + n;
-            if (active && g == 0 && head < a.H) a.delta_out[(size_t)t * a.H + head] = v;
-        }
-    }
-}
-
-template <int DQK, int NW, int NT>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_sdp_kernel(BwdArgs a) {
-    sdp_token<DQK, NW, NT, false>(a);
-}
-
-template <int DQK, int NW, int NT>
-__global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
-    sdp_token<DQK, NW, NT, true>(a);
-}
-
-// ---------------------------------------------------------------------------
-// bwd_dq: dQ^T = K^T (scale dS)^T for all heads of one token.  NW waves; wave
-// w owns NT x 16 heads and 1/CS of the d_qk columns (CS column groups, the
-// waves of one head group are adjacent): 32/CS main column tiles starting at a
-// multiple of 16 tiles, plus (d_qk = 576) 4/CS of the rope column tiles.
-// ---------------------------------------------------------------------------
-template <int DQK, int NW, int NT, int CS>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
-    using Tile = KvTileSwz<DQK>;
-    constexpr int MAIN_PER = Tile::MC_MAIN / CS;               // main column tiles per wave
-    constexpr int ROPE_PER = Tile::ROPE ? 4 / CS : 0;          // rope column tiles per wave
-    constexpr int MCW = MAIN_PER + ROPE_PER;
-    constexpr int HT = NW / CS * NT * 16;                      // heads per workgroup
-    static_assert(MAIN_PER % 8 == 0, "main tile groups must keep mc % 8 static");
-    __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
-    __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
-    __shared__ int s_rows[3][BLK];
-    __shared__ int s_live[3];
-    __shared__ int s_last[NW];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, n = lane & 15;
-    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
-    const int h_wave = (int)blockIdx.y * HT + (wave / CS) * NT * 16;
-    const int cgrp = wave % CS;
-    const int mcb = cgrp * MAIN_PER;                           // first main tile
-    const int rpb = cgrp * ROPE_PER;                           // first rope tile
-    const bool active = h_wave < a.H;
-    const int L = row_length(a.len, t, a.W);
-    const int nblk = (L + BLK - 1) / BLK;
-
-    f32x4 acc[MCW][NT];
-#pragma unroll
-    for (int mc = 0; mc < MCW; ++mc)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mc][nt] = zero4();
-    const typename Tile::Lane TL = Tile::lane_bases(lane);
-
-    // K^T operands of the wave's column tile k (slots 0..31 and 32..63)
-    auto kload = [&](const __bf16* tile, int k, bf16x8 (&dst)[2]) {
-        if (k < MAIN_PER) {
-            dst[0] = Tile::slot_op_main(tile, TL, 0, mcb + k);
-            dst[1] = Tile::slot_op_main(tile, TL, 32, mcb + k);
-        } else {
-            dst[0] = Tile::slot_op_rope(tile, TL, 0, rpb + k - MAIN_PER);
-            dst[1] = Tile::slot_op_rope(tile, TL, 32, rpb + k - MAIN_PER);
-        }
-    };
-
-    // (scale dS)^T as B operands: lane (g, n) holds 8 slots of head n in the
-    // slot order of slot_op: 32kk + 4g + j (j < 4), 32kk + 16 + 4g + j - 4.
-    // Loaded one block ahead (before that block's gather is issued) into the
-    // buffer of the block's parity.
-    bf16x8 dsop[2][2][NT];
-    auto load_ds = [&](int b, auto par) {
-        if (!active) return;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int head = h_wave + nt * 16 + n;
-            const bool hv = head < a.H;
-            const __bf16* src = a.ws_ds + ((size_t)(t - a.t0) * a.H + (hv ? head : 0)) * a.Wp + b * BLK + 4 * g;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                if (hv) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(src + 32 * kk);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 32 * kk + 16);
-                    dsop[par][kk][nt] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                } else {
-                    dsop[par][kk][nt] = zero8();
-                }
-            }
-        }
-    };
-
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
-                             wave, lane,
-                             [&](const __bf16* tile, const int* rows, int b, auto par, const auto& gs, bool live) {
-        (void)rows;
-        (void)b;
-        if (!active || !live) {
-            gs.all();
-            return;
-        }
-        static_assert(std::decay_t<decltype(gs)>::STEPS <= MCW, "the gather must fit in the column loop");
-        bf16x8 kop[2][2];
-        kload(tile, 0, kop[0]);
-#pragma unroll
-        for (int mc = 0; mc < MCW; ++mc) {
-            const int cur = mc & 1;
-            if (mc + 1 < MCW) kload(tile, mc + 1, kop[cur ^ 1]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                acc[mc][nt] = mfma16(kop[cur][0], dsop[par][0][nt], acc[mc][nt]);
-                acc[mc][nt] = mfma16(kop[cur][1], dsop[par][1][nt], acc[mc][nt]);
-            }
-            gs.step(mc);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }, load_ds);
-
-    if (!active) return;
-    if (a.nsplit > 1) {
-        // this split's share of dQ, in fp32, for dq_reduce_kernel
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int head = h_wave + nt * 16 + n;
-            if (head >= a.H) continue;
-            float* dp = a.dq_part + (((size_t)(t - a.t0) * a.nsplit + blockIdx.z) * a.H + head) * DQK + 4 * g;
-#pragma unroll
-            for (int mc = 0; mc < MCW; ++mc) {
-                const int col = mc < MAIN_PER ? 16 * (mcb + mc) : 16 * (Tile::MC_MAIN + rpb + mc - MAIN_PER);
-                *reinterpret_cast<f32x4*>(dp + col) = acc[mc][nt];
-            }
-        }
-        return;
-    }
+    // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+        float v = pdp[nt];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
         const int head = h_wave + nt * 16 + n;
-        if (head >= a.H) continue;
-        __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 4 * g;
-#pragma unroll
-        for (int mc = 0; mc < MCW; ++mc) {
-            const int col = mc < MAIN_PER ? 16 * (mcb + mc) : 16 * (Tile::MC_MAIN + rpb + mc - MAIN_PER);
-            st4(dqp + col, cvt4(acc[mc][nt][0], acc[mc][nt][1], acc[mc][nt][2], acc[mc][nt][3]));
-        }
+        if (active && g == 0 && head < a.H) a.delta_out[(size_t)t * a.H + head] = v;
     }
 }
 
@@ -782,6 +613,234 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
         for (; s < a.nsplit; ++s) acc += *reinterpret_cast<const f32x4*>(src + s * sstride + c);
         st4(a.dq + ((size_t)(a.t0 + tl) * a.H + h) * DQK + c, cvt4(acc[0], acc[1], acc[2], acc[3]));
     }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_sdq: S, P, dP, dS and dQ of 64 heads of one token in one pass over the
+// token's gathered blocks.  Four waves of 16 heads, one per SIMD: q and dO
+// (the B operands of S^T = K Q^T and dP^T = V dO^T) and the dQ^T accumulators
+// of all d_qk columns take about 300 registers per lane.  Per half block (32
+// slots) the wave forms P and scale dS in the C layout of its two 16-slot
+// S^T tiles, stores them for the dKV pass, and uses the same registers,
+// rounded to bf16, as the B operand of dQ^T += K^T (scale dS)^T: that C
+// layout is the slot order of KvTileSwz::slot_op, so dS reaches the dQ
+// product without a trip through LDS or memory, and the gathered tile serves
+// both products.  More than 64 heads take more workgroups per token
+// (blockIdx.y).
+// ---------------------------------------------------------------------------
+template <int DQK>
+__device__ __forceinline__ void sdq_block(const BwdArgs& a, const __bf16* tile,
+                                          const typename KvTileSwz<DQK>::Lane& TL, const int* rows,
+                                          const bf16x8 (&qop)[DQK / 32], const bf16x8 (&dop)[16], float lse2,
+                                          float dlt, f32x4 (&acc)[DQK / 16], int t, int head, int b, int lane,
+                                          const GatherSpread<DQK, 4>& gs) {
+    using Tile = KvTileSwz<DQK>;
+    constexpr int KS = DQK / 32, KV_ = 16, MC = DQK / 16;
+    static_assert(GatherSpread<DQK, 4>::STEPS <= KS, "the gather must fit in the first half's S loop");
+    const int g = lane >> 4;
+    const bool hv = head < a.H;
+
+    // The halves in the order S(0), S(1), dQ(0), dQ(1): the P / dS arithmetic
+    // of half 0 runs between the MFMAs of S(1) and that of half 1 between
+    // those of dQ(0), so that it overlaps matrix work (one wave per SIMD:
+    // nothing else would).  Each half's arithmetic and its order are unchanged.
+    f32x4 sacc[2][2], dpacc[2][2];              // [half][m]
+    // ok[h][k]: slot 32 h + 16 (k / 4) + 4g + k % 4 is valid (each half's
+    // flags are read from LDS right before that half's P / dS steps)
+    bool ok[2][8];
+    auto flags = [&](auto H) {
+        constexpr int h = decltype(H)::value;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ok[h][k] = rows[(2 * h + (k >> 2)) * 16 + 4 * g + (k & 3)] >= 0;
+    };
+
+    // S^T and dP^T for slots 32 h .. +31 (K operands two k-steps ahead: one
+    // wave per SIMD leaves the LDS latency to the wave's own prefetch); the
+    // first 16 k-steps (the V columns) also feed dP; step(ks) runs after each
+    // k-step's MFMAs
+    auto s_loop = [&](auto H, auto&& step) {
+        constexpr int h = decltype(H)::value;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) { sacc[h][m] = zero4(); dpacc[h][m] = zero4(); }
+        constexpr int SA = 2;
+        bf16x8 kop[SA + 1][2];
+#pragma unroll
+        for (int k = 0; k < SA; ++k)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) kop[k][m] = Tile::row_op(tile, TL, (2 * h + m) * 16, k);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + SA < KS) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    kop[(ks + SA) % (SA + 1)][m] = Tile::row_op(tile, TL, (2 * h + m) * 16, ks + SA);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                sacc[h][m] = mfma16(kop[ks % (SA + 1)][m], qop[ks], sacc[h][m]);
+                if (ks < KV_) dpacc[h][m] = mfma16(kop[ks % (SA + 1)][m], dop[ks], dpacc[h][m]);
+            }
+            step(ks);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // value k (0..7) of half h: P = 2^(s * scale * log2 e - LSE_tot * log2 e),
+    // masked; dS' = scale P (dP - Delta).  P replaces S, dS' replaces dP.
+    auto epi_step = [&](auto H, int k) {
+        constexpr int h = decltype(H)::value;
+        const int m = k >> 2, i = k & 3;
+        const float p = ok[h][k] ? fast_exp2(sacc[h][m][i] * a.scale_log2 - lse2) : 0.f;
+        sacc[h][m][i] = p;
+        dpacc[h][m][i] = p * (dpacc[h][m][i] - dlt) * a.scale;
+    };
+
+    // bf16 P and dS' of half h: stored for the dKV pass; dS' returned as the B
+    // operand of dQ^T (lane (g, n) holds slots 32 h + 4g + j and
+    // 32 h + 16 + 4g + j of head n, the order of slot_op)
+    auto finish = [&](auto H) {
+        constexpr int h = decltype(H)::value;
+        const bf16x4 ds_lo = cvt4(dpacc[h][0][0], dpacc[h][0][1], dpacc[h][0][2], dpacc[h][0][3]);
+        const bf16x4 ds_hi = cvt4(dpacc[h][1][0], dpacc[h][1][1], dpacc[h][1][2], dpacc[h][1][3]);
+        if (hv) {
+            const size_t base = ((size_t)(t - a.t0) * a.H + head) * a.Wp + b * BLK + h * 32 + 4 * g;
+            st4(a.ws_p + base, cvt4(sacc[h][0][0], sacc[h][0][1], sacc[h][0][2], sacc[h][0][3]));
+            st4(a.ws_p + base + 16, cvt4(sacc[h][1][0], sacc[h][1][1], sacc[h][1][2], sacc[h][1][3]));
+            st4(a.ws_ds + base, ds_lo);
+            st4(a.ws_ds + base + 16, ds_hi);
+        }
+        return cat44(ds_lo, ds_hi);
+    };
+
+    // dQ^T += K^T (scale dS)^T over slots 32 h .. +31, K^T operands DA column
+    // tiles ahead; step(mc) runs after each column tile's MFMA
+    auto dq_loop = [&](auto H, bf16x8 dsb, auto&& step) {
+        constexpr int h = decltype(H)::value;
+        constexpr int DA = 4;
+        bf16x8 kt[DA + 1];
+#pragma unroll
+        for (int k = 0; k < DA; ++k) kt[k] = Tile::slot_op(tile, TL, 32 * h, k);
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+            if (mc + DA < MC) kt[(mc + DA) % (DA + 1)] = Tile::slot_op(tile, TL, 32 * h, mc + DA);
+            acc[mc] = mfma16(kt[mc % (DA + 1)], dsb, acc[mc]);
+            step(mc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    s_loop(H0{}, [&](int ks) { gs.step(ks); });
+    flags(H0{});
+    s_loop(H1{}, [&](int ks) {
+        if (ks < 8) epi_step(H0{}, ks);
+    });
+    const bf16x8 dsb0 = finish(H0{});
+    flags(H1{});
+    dq_loop(H0{}, dsb0, [&](int mc) {
+        if (mc < 8) epi_step(H1{}, mc);
+    });
+    const bf16x8 dsb1 = finish(H1{});
+    dq_loop(H1{}, dsb1, [](int) {});
+}
+
+template <int DQK>
+__global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
+    using Tile = KvTileSwz<DQK>;
+    constexpr int NW = 4, KS = DQK / 32, MC = DQK / 16, HT = NW * 16;
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile0[Tile::ELEMS];
+    __shared__ __attribute__((aligned(16))) __bf16 s_tile1[Tile::ELEMS];
+    __shared__ int s_rows[3][BLK];
+    __shared__ int s_live[3];
+    __shared__ int s_last[NW];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, n = lane & 15;
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
+    const int h_wave = (int)blockIdx.y * HT + wave * 16;
+    const int head = h_wave + n;
+    const bool hv = head < a.H;
+    const bool active = h_wave < a.H;
+    const int L = row_length(a.len, t, a.W);
+    const int nblk = (L + BLK - 1) / BLK;
+
+    f32x4 acc[MC];
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) acc[mc] = zero4();
+
+    if (nblk == 0) {
+        // an empty row: dQ = 0 below; Delta = O dO still when it is formed here
+        if (a.o != nullptr && active) {
+            float unused[1];
+            fused_delta<1>(a, t, h_wave, lane,
+                           [&](int, int ks, size_t row) { return ld8(a.dO + row * 512 + 32 * ks + 8 * g); },
+                           unused);
+        }
+    } else {
+        // q, dO (and the LSE, Delta scalars) go to registers once the first
+        // tile's gather is in flight; with o given, Delta = sum O dO is formed
+        // from dO before q is loaded
+        // The LSE, sink and Delta scalars load first; q and dO go out right
+        // behind the row's first indices (early), so that the wait for those
+        // indices does not wait for them; their arithmetic waits until the
+        // first tile's gather is in flight (post).  With o given, Delta =
+        // sum O dO is formed there from dO and O.  Lanes of heads past H load
+        // head 0's row (the loads stay unconditional: the compiler loses
+        // count of loads issued inside a branch and would then drain them at
+        // the indices' wait) and zero it.
+        bf16x8 qop[KS], dop[16];
+        const size_t row = (size_t)t * a.H + (hv ? head : 0);
+        const float l_raw = a.lse[row];
+        const float sk_raw = a.sink ? a.sink[hv ? head : 0] : 0.f;
+        float lse2 = 0.f, dlt = a.o == nullptr ? a.delta[row] : 0.f;
+        auto early = [&]() {
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8 x = ld8(a.dO + row * 512 + 32 * ks + 8 * g);
+                dop[ks] = hv ? x : zero8();
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 x = ld8(a.q + row * DQK + 32 * ks + 8 * g);
+                qop[ks] = hv ? x : zero8();
+            }
+        };
+        auto post = [&]() {
+            // +inf for a saturating sink: every P is 0
+            lse2 = hv ? (a.sink ? glae(l_raw, sk_raw) : l_raw) * LOG2E : 0.f;
+            if (!hv) dlt = 0.f;
+            if (a.o != nullptr && active) {     // uniform
+                float d1[1];
+                fused_delta<1>(a, t, h_wave, lane, [&](int, int ks, size_t) { return dop[ks]; }, d1);
+                dlt = d1[0];
+            }
+        };
+        const typename Tile::Lane TL = Tile::lane_bases(lane);
+        gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
+                                 wave, lane,
+                                 [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
+                                     if (active && live)
+                                         sdq_block<DQK>(a, tile, TL, rows, qop, dop, lse2, dlt, acc, t, head, b,
+                                                        lane, gs);
+                                     else
+                                         gs.all();
+                                 }, NoPre{}, post, early);
+    }
+
+    if (!hv) return;
+    if (a.nsplit > 1) {
+        // this split's share of dQ, in fp32, for dq_reduce_kernel
+        float* dp = a.dq_part + (((size_t)(t - a.t0) * a.nsplit + blockIdx.z) * a.H + head) * DQK + 4 * g;
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) *reinterpret_cast<f32x4*>(dp + 16 * mc) = acc[mc];
+        return;
+    }
+    __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 4 * g;
+#pragma unroll
+    for (int mc = 0; mc < MC; ++mc) st4(dqp + 16 * mc, cvt4(acc[mc][0], acc[mc][1], acc[mc][2], acc[mc][3]));
 }
 
 // ---------------------------------------------------------------------------
@@ -1187,8 +1246,8 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
     if (threadIdx.x == 0) d_sink[h] = -s_part[0];
 }
 
-// stage boundaries: 0 start | 1 index inversion | 2 sdp | 3 dq | 4 dkv |
-// 5 reduce | 6 d_sink.  With several token chunks, events 1-5 are recorded
+// stage boundaries: 0 start | 1 index inversion | 2 S/dP and dQ | 3 dQ merge
+// (split block ranges) | 4 dkv | 5 reduce | 6 d_sink.  With several token chunks, events 1-5 are recorded
 // during the first chunk only (they bracket its stages) and event 6 after the
 // whole call.
 struct Marks {
@@ -1239,15 +1298,8 @@ static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Mar
     // sdp: 16 heads per wave keep q and dO (the B operands) within half the
     // register file, so two waves share each SIMD and hide each other's
     // gather and LDS latency; 8 such waves cover 128 heads.
-    if (a.H > 64) {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 8, 1>), dim3(a.Tc, 1, ns), dim3(512), 0, stream, a);
-        mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 8, 2, 2>), dim3(a.Tc, 1, ns), dim3(512), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL((bwd_sdp_kernel<DQK, 4, 1>), dim3(a.Tc, 1, ns), dim3(256), 0, stream, a);
-        mark(2);
-        hipLaunchKernelGGL((bwd_dq_kernel<DQK, 4, 1, 1>), dim3(a.Tc, 1, ns), dim3(256), 0, stream, a);
-    }
+    hipLaunchKernelGGL((bwd_sdq_kernel<DQK>), dim3(a.Tc, (a.H + 63) / 64, ns), dim3(256), 0, stream, a);
+    mark(2);
     if (ns > 1)
         hipLaunchKernelGGL((dq_reduce_kernel<DQK>), dim3((a.Tc * a.H + 3) / 4), dim3(256), 0, stream, a);
     mark(3);
@@ -1264,7 +1316,7 @@ static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Mar
     return hipSuccess;
 }
 
-// Exact Delta: the S / dP half of bwd_sdp, accumulating sum_j P_j dP_j
+// Exact Delta: the S / dP half of bwd_sdq, accumulating sum_j P_j dP_j
 // instead of storing P and dS.
 template <int DQK>
 static void launch_delta_exact_t(const BwdArgs& a, hipStream_t stream) {

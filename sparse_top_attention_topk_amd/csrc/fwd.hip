@@ -285,22 +285,39 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 
     // The row's last valid slot: the blocks after its block hold padding only
     // (the tail of a non-compact row), so the block loop ends there.  Each
-    // wave's maximum goes to s_last, read after the first barrier below.
+    // wave's maximum goes to s_last, read after the first barrier below.  The
+    // raw indices of the range's first 4 x NW x 64 slots and of its second
+    // block load in one batch with q: the slot rows of the first block are
+    // v[0] of threads 0..63, those of the second block row1.
+    static_assert(NTH >= 2 * BLK, "the first index batch must cover two blocks");
+    int row0, row1;
     {
-        int last = -1;
-        for (int j0 = b_lo * BLK; j0 < j_hi; j0 += 4 * NTH) {
-            int v[4];
+        const int j_first = b_lo * BLK;
+        int v[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = raw_index(a, t, j0 + k * NTH + tid);
+        for (int k = 0; k < 4; ++k) v[k] = raw_index(a, t, j_first + k * NTH + tid);
+        row1 = raw_index(a, t, j_first + BLK + (tid & (BLK - 1)));
+        int last = -1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = j_first + k * NTH + tid;
+            if (valid_row(v[k], j, j_hi, a.S_kv) >= 0) last = j;
+        }
+        for (int j0 = j_first + 4 * NTH; j0 < j_hi; j0 += 4 * NTH) {     // rows longer than one batch
+            int u[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) u[k] = raw_index(a, t, j0 + k * NTH + tid);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int j = j0 + k * NTH + tid;
-                if (valid_row(v[k], j, j_hi, a.S_kv) >= 0) last = j;
+                if (valid_row(u[k], j, j_hi, a.S_kv) >= 0) last = j;
             }
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) last = max(last, __shfl_xor(last, m, 64));
         if (lane == 0) s_last[wave] = last;
+        row0 = valid_row(v[0], j_first + (tid & (BLK - 1)), j_hi, a.S_kv);
+        row1 = valid_row(row1, j_first + BLK + (tid & (BLK - 1)), j_hi, a.S_kv);
     }
     int nblk = 0;
 
@@ -313,8 +330,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
         for (int nt = 0; nt < NT; ++nt) { rmax[nt] = -INFINITY; l_run[nt] = 0.f; l_rnd[nt] = 0.f; }
 
         if (tid < BLK) {
-            s_rows[0][tid] = slot_row(a.idx, t, a.W, j_hi, a.S_kv, b_lo * BLK + tid);
-            s_rows[1][tid] = slot_row(a.idx, t, a.W, j_hi, a.S_kv, (b_lo + 1) * BLK + tid);
+            s_rows[0][tid] = row0;
+            s_rows[1][tid] = row1;
             s_rows[2][tid] = -1;     // written again before any block reads it
         }
         __syncthreads();
