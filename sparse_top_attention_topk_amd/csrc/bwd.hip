@@ -848,8 +848,9 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
 //   u[slot][c] = sum_h (scale dS)[h][slot] q[h][c] + P[h][slot] dO[h][c]
 // computed as u^T = q^T (scale dS) + dO^T P, a contraction over heads (HK
 // k-steps of 32 heads).  Eight waves (two per SIMD, so one wave's stores
-// overlap the other's MFMAs) split the 16-column tiles of d_qk: 5 or 4 each
-// for d_qk = 576, 4 each for 512.
+// overlap the other's MFMAs) split the 16-column tiles of d_qk: four d_v
+// tiles each (q dS + dO P), and for d_qk = 576 one of the four rope tiles
+// (q dS only) for each of the first four waves.
 // q and dO for those columns stay in registers with heads in-lane, staged once
 // per token through LDS with asynchronous loads (two buffers in flight).  The
 // P / dS tiles of the next block load asynchronously while the current block
@@ -951,13 +952,12 @@ __device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int 
     return cat44(lds_tr4(tile + e0), lds_tr4(tile + e1));
 }
 
-template <int DQK, int HK, int NTC>
+template <int DQK, int HK, int MW, int RW, bool ROPE>
 __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, const int* raw,
-                                          const bf16x8 (&qB)[HK][NTC],
-                                          const bf16x8 (&dB)[HK][NTC], int b, int L,
-                                          __amdgpu_buffer_rsrc_t prs, int voff, int ntc, int lane) {
+                                          const bf16x8 (&qB)[HK][MW + RW], const bf16x8 (&dB)[HK][MW], int b,
+                                          int L, __amdgpu_buffer_rsrc_t prs, int voff, int voff_rope, int lane) {
     constexpr int HP = 32 * HK;
-    const int g = lane >> 4, n = lane & 15;
+    const int n = lane & 15;
     {
         // a block without a valid slot writes nothing (and its P / dS tile
         // was never stored): skip it
@@ -967,32 +967,32 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
     // four quarters of 16 slots: one accumulator tile per column tile
 #pragma unroll
     for (int qt = 0; qt < 4; ++qt) {
-        f32x4 acc[NTC];
+        f32x4 acc[MW + 1];
 #pragma unroll
-        for (int nt = 0; nt < NTC; ++nt) acc[nt] = zero4();
+        for (int nt = 0; nt <= MW; ++nt) acc[nt] = zero4();
 #pragma unroll
         for (int hk = 0; hk < HK; ++hk) {
             const bf16x8 bp = pd_op(pd, 32 * hk, 16 * qt, lane);
             const bf16x8 bds = pd_op(pd + HP * BLK, 32 * hk, 16 * qt, lane);
 #pragma unroll
-            for (int nt = 0; nt < NTC; ++nt) {
-                // dB is zero for columns past d_v: unconditional, so the MFMAs
-                // stay in one basic block for the scheduler
+            for (int nt = 0; nt < MW; ++nt) {
                 acc[nt] = mfma16(qB[hk][nt], bds, acc[nt]);
                 acc[nt] = mfma16(dB[hk][nt], bp, acc[nt]);
             }
+            // a rope column tile: q dS only (dO has no columns there)
+            if constexpr (ROPE) acc[MW] = mfma16(qB[hk][MW], bds, acc[MW]);
         }
-        // lane (g, n) holds columns c_wave + 16nt + 4g .. +3 of slot 16 qt + n,
-        // stored as one 4-value block (8 bytes); only valid slots are written
-        // (the row lists name no other slot)
+        // lane (g, n) holds columns c + 4g .. +3 of slot 16 qt + n for each of
+        // its column tiles, stored as one 4-value block (8 bytes); only valid
+        // slots are written (the row lists name no other slot)
         const int slot = 16 * qt + n;
         const int v = raw[slot];
         if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
             const int soff = (b * BLK + 16 * qt) * (2 * DQK);
 #pragma unroll
-            for (int nt = 0; nt < NTC; ++nt)
-                if (NTC * 8 == DQK / 16 || nt < ntc)            // the wave's own tiles
-                    __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[nt]), prs, voff + 32 * nt, soff, 0);
+            for (int nt = 0; nt < MW; ++nt)
+                __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[nt]), prs, voff + 32 * nt, soff, 0);
+            if constexpr (ROPE) __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[MW]), prs, voff_rope, soff, 0);
         }
     }
 }
@@ -1001,9 +1001,10 @@ template <int DQK, int HK>
 __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int DV = 512;
     constexpr int NW = 8;
-    constexpr int NTILES = DQK / 16;                    // 16-column tiles (36 or 32)
-    constexpr int NTC = (NTILES + NW - 1) / NW;         // tiles per wave, at most (5 or 4)
-    constexpr int R = NTILES - NW * (NTC - 1);          // waves that take NTC tiles
+    constexpr int MW = DV / 16 / NW;                    // main (d_v) column tiles per wave: 4
+    constexpr int RW = (DQK - DV) / 16 > 0 ? 1 : 0;     // a rope column tile, for the first RN waves
+    constexpr int RN = (DQK - DV) / 16;                 // rope column tiles (4 or 0)
+    static_assert(RN <= NW, "one rope column tile per wave at most");
     constexpr int HP = 32 * HK;                         // heads padded
     // four LDS buffers of one size: s_st0, s_st1 and s_pd1 take the staged
     // q / dO pieces in turn (three in flight); afterwards s_pd0 / s_pd1 hold
@@ -1025,12 +1026,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int b_lo = a.nsplit > 1 ? (int)blockIdx.z * a.bps : 0;
     const int b_end = a.nsplit > 1 && b_lo + a.bps < nblk ? b_lo + a.bps : nblk;
     if (b_end <= b_lo) return;             // uniform: an empty row (or range) adds nothing
-    // wave w owns tiles [tile0, tile0 + ntc): the first R waves NTC tiles, the
-    // rest NTC - 1 (their last tile slot is computed on zero operands and not
-    // stored)
-    const int tile0 = wave < R ? wave * NTC : R * NTC + (wave - R) * (NTC - 1);
-    const int ntc = wave < R ? NTC : NTC - 1;
-    const int c_wave = 16 * tile0;
+    // wave w owns main column tiles [MW w, MW w + MW) (columns 64 w ..) and,
+    // for w < RN, rope column tile w (columns 512 + 16 w ..): every MFMA has
+    // real operands, and the two waves of a SIMD issue 9 + 8 of them per
+    // 32-head step
+    const int c_wave = 16 * MW * wave;
+    const bool has_rope = RW > 0 && wave < RN;           // uniform
+    const int c_rope = DV + 16 * wave;
 
     // heads past H: their P / dS tile rows stay zero (never loaded; s_pd1 is
     // cleared after its turn as a staging buffer)
@@ -1043,12 +1045,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     if (HP > a.H) zero_rows_past_h(s_pd0);
 
     // ---- q and dO with heads in-lane: lane (g, n) of k-step hk, column tile
-    // nt holds X[32hk + 8g + j][c_wave + 16nt + n], j = 0..7.  Staged in 2*HK
+    // nt holds X[32hk + 8g + j][c + n], j = 0..7, c the tile's first column
+    // (c_wave + 16 nt, or c_rope for the rope tile nt = MW).  Staged in 2*HK
     // pieces of 32 head rows (rows past H repeat row H-1: their P and dS are
     // zero) through a ring of three buffers: piece p + 2 loads while piece p
     // is read and piece p + 1 lands.  The [P | dS] tile of block 0 loads first
     // (into s_pd0, outside the ring), so it is there when the pieces are.
-    bf16x8 qB[HK][NTC], dB[HK][NTC];
+    bf16x8 qB[HK][MW + RW], dB[HK][MW];
     constexpr int NPC = 2 * HK;
     __bf16* const ring[3] = {s_st0, s_st1, s_pd1};
     auto issue = [&](int piece) {
@@ -1086,15 +1089,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         // operands are read unconditionally (column clamped into the piece)
         // and zeroed after: no branch around the LDS reads
 #pragma unroll
-        for (int nt = 0; nt < NTC; ++nt) {
+        for (int nt = 0; nt < MW; ++nt) {
             const int c0 = c_wave + 16 * nt;
-            if ((piece & 1) == 0) {
-                const bf16x8 x = stage_op<DQK>(cur, c0 < DQK ? c0 : 0, lane);
-                qB[hk][nt] = nt < ntc ? x : zero8();
-            } else {
-                const bf16x8 x = stage_op<DV>(cur, c0 < DV ? c0 : 0, lane);
-                dB[hk][nt] = nt < ntc && c0 < DV ? x : zero8();
-            }
+            if ((piece & 1) == 0) qB[hk][nt] = stage_op<DQK>(cur, c0, lane);
+            else dB[hk][nt] = stage_op<DV>(cur, c0, lane);
+        }
+        // the rope tile's q (read by every wave, the column clamped into the
+        // piece, and zeroed where the wave has none: no branch around the
+        // LDS read)
+        if (RW > 0 && (piece & 1) == 0) {
+            const bf16x8 x = stage_op<DQK>(cur, RW > 0 && wave < RN ? c_rope : 0, lane);
+            qB[hk][MW + RW - 1] = has_rope ? x : zero8();
         }
     }
     // Every wave must be done reading the last staged piece before s_pd1's
@@ -1107,11 +1112,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
     // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
-    // slot 16 qt + n, columns c_wave + 16 nt + 4g .. +3
+    // slot 16 qt + n, columns c + 4g .. +3 of each of its column tiles
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
         0x00020000);
     const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 4 * (lane >> 4));
+    const int voff_rope = (lane & 15) * (2 * DQK) + 2 * (c_rope + 4 * (lane >> 4));
+    // one copy of the block per kind of wave, so the MFMAs stay in one basic block
+    auto block = [&](const __bf16* pd, const int* raw, int b) __attribute__((always_inline)) {
+        if (has_rope)
+            dkv_block<DQK, HK, MW, RW, RW != 0>(a, pd, raw, qB, dB, b, L, prs, voff, voff_rope, lane);
+        else
+            dkv_block<DQK, HK, MW, RW, false>(a, pd, raw, qB, dB, b, L, prs, voff, voff_rope, lane);
+    };
     for (int b = b_lo; b < b_end; b += 2) {
         wait_vmem();
         __syncthreads();
@@ -1119,7 +1132,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
         }
-        dkv_block<DQK, HK, NTC>(a, s_pd0, s_raw[0], qB, dB, b, L, prs, voff, ntc, lane);
+        block(s_pd0, s_raw[0], b);
         if (b + 1 >= b_end) break;
         wait_vmem();
         __syncthreads();
@@ -1127,7 +1140,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
         }
-        dkv_block<DQK, HK, NTC>(a, s_pd1, s_raw[1], qB, dB, b + 1, L, prs, voff, ntc, lane);
+        block(s_pd1, s_raw[1], b + 1);
     }
 }
 
