@@ -222,6 +222,102 @@ __global__ __launch_bounds__(1024) void rows_scan_kernel(BwdArgs a) {
     }
 }
 
+// The whole inversion in one workgroup, for chunks of few slots (decode,
+// short prefixes) where the five launches above are mostly launch latency:
+// counts in LDS over all of the chunk's slots at once, the two exclusive
+// scans with the part -> row map, then the row lists in token order (a
+// barrier after each token; the next token's slot rows load while the
+// current one is placed).  Same lists, offsets and parts as the five kernels.
+// Needs S_kv <= INV_ROWS (the counters in LDS) and W <= SMALL_INV_W; taken
+// for at most SMALL_INV_TOKENS tokens (each token costs a barrier: measured,
+// 64 tokens of 32 slots took 31 us here against 20 us in the five kernels,
+// one token of 1152 slots 24 against 53 us, 16 tokens 46 against 57 us).
+constexpr int SMALL_INV_TOKENS = 16;
+constexpr int SMALL_INV_W = 4096;            // slots of a token held by the 1024 threads
+
+__global__ __launch_bounds__(1024) void rows_small_kernel(BwdArgs a) {
+    extern __shared__ int s_c[];             // [S_kv]: counts, then cursors
+    __shared__ int s_w[2][16];
+    const int n = a.S_kv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < n; i += 1024) s_c[i] = 0;
+    __syncthreads();
+    {
+        const int total = a.Tc * a.W;
+        for (int i0 = 0; i0 < total; i0 += 4 * 1024) {
+            int r[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * 1024 + tid;
+                const int tl = i / a.W;
+                const int t = a.t0 + (tl < a.Tc ? tl : a.Tc - 1);
+                r[u] = i < total ? slot_row(a.idx, t, a.W, row_length(a.len, t, a.W), n, i - tl * a.W) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (r[u] >= 0) atomicAdd(s_c + r[u], 1);
+        }
+    }
+    __syncthreads();
+    // tiles of 8192 rows, 8 per thread (as rows_scan_kernel, from LDS)
+    int carry = 0, carry2 = 0;
+    for (int base = 0; base < n; base += 8192) {
+        const int r0 = base + 8 * tid;
+        int c[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) c[k] = r0 + k < n ? s_c[r0 + k] : 0;
+        int sum = 0, sum2 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { sum += c[k]; sum2 += nparts(c[k]); }
+        const int inc = wave_incl_scan(sum, lane), inc2 = wave_incl_scan(sum2, lane);
+        if (lane == 63) { s_w[0][wave] = inc; s_w[1][wave] = inc2; }
+        __syncthreads();
+        int wpre = 0, wpre2 = 0, tot = 0, tot2 = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int v = s_w[0][w], v2 = s_w[1][w];
+            if (w < wave) { wpre += v; wpre2 += v2; }
+            tot += v; tot2 += v2;
+        }
+        int run = carry + wpre + inc - sum, run2 = carry2 + wpre2 + inc2 - sum2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (r0 + k < n) {
+                a.row_off[r0 + k] = run;
+                a.part_off[r0 + k] = run2;
+                s_c[r0 + k] = run;                   // the row's cursor
+                for (int q = 0; q < nparts(c[k]); ++q) a.part_row[run2 + q] = r0 + k;
+            }
+            run += c[k];
+            run2 += nparts(c[k]);
+        }
+        carry += tot;
+        carry2 += tot2;
+        __syncthreads();                       // s_w is reused by the next tile
+    }
+    if (tid == 0) {
+        a.row_off[n] = carry;
+        a.part_off[n] = carry2;
+    }
+    // slots j = tid + 1024 u of token t (u < 4 covers W <= SMALL_INV_W)
+    auto rows_of = [&](int t, int (&r)[4]) {
+        const int L = row_length(a.len, t, a.W);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = slot_row(a.idx, t, a.W, L, n, u * 1024 + tid);
+    };
+    int cur[4], nxt[4] = {-1, -1, -1, -1};
+    rows_of(a.t0, cur);
+    for (int t = a.t0; t < a.t0 + a.Tc; ++t) {
+        if (t + 1 < a.t0 + a.Tc) rows_of(t + 1, nxt);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (cur[u] >= 0) a.entries[atomicAdd(s_c + cur[u], 1)] = (t - a.t0) * a.Wp + u * 1024 + tid;
+        __syncthreads();                       // token order
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    }
+}
+
 // part -> row map for the reduce
 __global__ __launch_bounds__(256) void rows_parts_kernel(BwdArgs a) {
     const int r = (int)blockIdx.x * 256 + threadIdx.x;
@@ -1279,6 +1375,13 @@ struct Marks {
 static hipError_t launch_inversion(const BwdArgs& a, hipStream_t stream) {
     const int nr = a.S_kv < INV_ROWS ? a.S_kv : INV_ROWS;
     const size_t lds = (size_t)nr * sizeof(int);
+    if (a.S_kv <= INV_ROWS && a.W <= SMALL_INV_W && a.Tc <= SMALL_INV_TOKENS) {
+        const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_small_kernel),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(rows_small_kernel, dim3(1), dim3(1024), lds, stream, a);
+        return hipSuccess;
+    }
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(rows_count_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err == hipSuccess)

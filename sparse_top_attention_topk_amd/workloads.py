@@ -198,6 +198,19 @@ def make_edge_width118(H, seed=40, T=64, S=128):
                    torch.from_numpy(idx), None, s, meta=dict(seed=seed))
 
 
+def make_deep_rows(T, seed=130, S=8, H=16, W=512):
+    """Every slot of every token names one of a few KV rows (drawn with
+    replacement from S = 8 rows, non-compact, with a sink): each row's list
+    holds about T * W / S entries, cut into several reduce parts, and a token
+    names each row dozens of times."""
+    rng = np.random.default_rng(seed + T)
+    dqk, dv = 576, 512
+    q, kv, dO, s = _dense(rng, T, S, H, dqk, dv, True)
+    idx = rng.integers(0, S, size=(T, W)).astype(np.int32)
+    return Problem(f"deep_rows_T{T}", T, S, H, dqk, dv, W, 1.0 / math.sqrt(dqk), q, kv, dO,
+                   torch.from_numpy(idx), None, s, meta=dict(seed=seed + T))
+
+
 DEGENERATE_KINDS = ("single", "all_invalid", "out_of_range", "duplicates")
 
 

@@ -322,6 +322,21 @@ def test_chunked_backward(name):
     assert not errors, f"{name}: " + "; ".join(errors)
 
 
+@pytest.mark.parametrize("T", (1, 16, 48))
+def test_deep_row_lists(T):
+    """A few KV rows named by every slot (each row's list several reduce parts
+    long, every token naming each row dozens of times), against the oracle:
+    chunks of up to 16 tokens take the one-workgroup index inversion, larger
+    ones the five-kernel one (T = 48, and T = 48 run in chunks of 16)."""
+    p = wl.make_deep_rows(T)
+    say(f"[gpu] deep rows T={T}: S_kv={p.S_kv} H={p.H} W={p.W}")
+    ref = run_oracle(p)
+    errors = compare_full(run_gpu(p, DEV), ref)
+    if T > 16:
+        errors += [f"chunks of 16: {e}" for e in compare_full(run_gpu(p, DEV, ws_tokens=16), ref)]
+    assert not errors, f"deep rows T={T}: " + "; ".join(errors)
+
+
 def test_batched_large_kv_set():
     """Three sequences whose concatenated KV set (43000 rows) is larger than
     one workgroup's inversion counters cover (32768 rows): O, LSE, dQ and
