@@ -855,8 +855,16 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, n = lane & 15;
-    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
-    const int h_wave = (int)blockIdx.y * HT + wave * 16;
+    // workgroup x -> (token, head group): the head groups of a token are 8
+    // workgroups apart, so that they run on one XCD (workgroups go to the 8
+    // XCDs in turn) at about the same time and the second gathers its rows
+    // from that XCD's L2; tokens the chunk's longest rows first
+    const int ngrp = (a.H + HT - 1) / HT;
+    const int blk = (int)blockIdx.x / (8 * ngrp), rem = (int)blockIdx.x % (8 * ngrp);
+    const int ti = blk * 8 + rem % 8;
+    if (ti >= a.Tc) return;                            // uniform: past the chunk's tokens
+    const int t = a.t0 + a.Tc - 1 - ti;
+    const int h_wave = (rem / 8) * HT + wave * 16;
     const int head = h_wave + n;
     const bool hv = head < a.H;
     const bool active = h_wave < a.H;
@@ -1414,7 +1422,8 @@ static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Mar
     // sdp: 16 heads per wave keep q and dO (the B operands) within half the
     // register file, so two waves share each SIMD and hide each other's
     // gather and LDS latency; 8 such waves cover 128 heads.
-    hipLaunchKernelGGL((bwd_sdq_kernel<DQK>), dim3(a.Tc, (a.H + 63) / 64, ns), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_sdq_kernel<DQK>), dim3((a.Tc + 7) / 8 * 8 * ((a.H + 63) / 64), 1, ns), dim3(256), 0,
+                       stream, a);
     mark(2);
     if (ns > 1)
         hipLaunchKernelGGL((dq_reduce_kernel<DQK>), dim3((a.Tc * a.H + 3) / 4), dim3(256), 0, stream, a);
