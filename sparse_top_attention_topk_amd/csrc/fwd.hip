@@ -266,16 +266,25 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 
     if (tid == 0) s_rerun = 0;
 
-    // Q as the B operand of S^T = K Q^T: lane (g, n) holds q[t, head, 32ks+8g..+7]
+    // Q as the B operand of S^T = K Q^T: lane (g, n) holds q[t, head, 32ks+8g..+7].
+    // Loaded right behind the row's first indices (below), so that the wait
+    // for those indices does not wait for q; unconditional loads (lanes of
+    // heads past H read head 0's row and zero it), since the compiler loses
+    // count of loads issued inside a branch and would drain them at that wait.
     bf16x8 qop[NT][C::KS];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int head = h_wave + nt * 16 + n;
-        const bool hv = head < a.H && L > 0;
-        const __bf16* qp = a.q + ((size_t)t * a.H + (hv ? head : 0)) * DQK + 8 * g;
+        for (int nt = 0; nt < NT; ++nt) {
+            const int head = h_wave + nt * 16 + n;
+            const bool hv = head < a.H && L > 0;
+            const __bf16* qp = a.q + ((size_t)t * a.H + (hv ? head : 0)) * DQK + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qop[nt][ks] = hv ? ld8(qp + 32 * ks) : zero8();
-    }
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const bf16x8 x = ld8(qp + 32 * ks);
+                qop[nt][ks] = hv ? x : zero8();
+            }
+        }
+    };
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     f32x4 oacc[C::MC][NT];
@@ -287,8 +296,8 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
     // (the tail of a non-compact row), so the block loop ends there.  Each
     // wave's maximum goes to s_last, read after the first barrier below.  The
     // raw indices of the range's first 4 x NW x 64 slots and of its second
-    // block load in one batch with q: the slot rows of the first block are
-    // v[0] of threads 0..63, those of the second block row1.
+    // block load in one batch, q behind them: the slot rows of the first
+    // block are v[0] of threads 0..63, those of the second block row1.
     static_assert(NTH >= 2 * BLK, "the first index batch must cover two blocks");
     int row0, row1;
     {
@@ -297,6 +306,9 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = raw_index(a, t, j_first + k * NTH + tid);
         row1 = raw_index(a, t, j_first + BLK + (tid & (BLK - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+        load_q();
+        __builtin_amdgcn_sched_barrier(0);
         int last = -1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
