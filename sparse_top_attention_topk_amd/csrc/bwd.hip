@@ -640,26 +640,45 @@ __global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
         return;
     }
 
-    // q, dO and the LSE go to registers once the first tile's gather is in
-    // flight
+    // The LSE and sink scalars load first; q and dO go out right behind the
+    // row's first indices (early), unconditionally (lanes of heads past H
+    // read head 0's row and zero it: the compiler loses count of loads issued
+    // inside a branch), so that the wait for those indices does not wait for
+    // them; the LSE arithmetic waits until the first tile's gather is in
+    // flight (post).
     bf16x8 qop[NT][KS], dop[NT][16];
-    float lse2[NT];
-    auto post = [&]() {
+    float lse2[NT], l_raw[NT], sk_raw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int head = h_wave + nt * 16 + n;
+        const bool hv = head < a.H;
+        l_raw[nt] = a.lse[(size_t)t * a.H + (hv ? head : 0)];
+        sk_raw[nt] = a.sink ? a.sink[hv ? head : 0] : 0.f;
+    }
+    auto early = [&]() {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int head = h_wave + nt * 16 + n;
             const bool hv = head < a.H;
             const size_t row = (size_t)t * a.H + (hv ? head : 0);
 #pragma unroll
-            for (int ks = 0; ks < 16; ++ks) dop[nt][ks] = hv ? ld8(a.dO + row * 512 + 32 * ks + 8 * g) : zero8();
-            lse2[nt] = 0.f;
-            if (hv) {
-                const float l = a.lse[row];
-                const float lt = a.sink ? glae(l, a.sink[head]) : l;
-                lse2[nt] = lt * LOG2E;     // +inf for a saturating sink: every P is 0
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8 x = ld8(a.dO + row * 512 + 32 * ks + 8 * g);
+                dop[nt][ks] = hv ? x : zero8();
             }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) qop[nt][ks] = hv ? ld8(a.q + row * DQK + 32 * ks + 8 * g) : zero8();
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 x = ld8(a.q + row * DQK + 32 * ks + 8 * g);
+                qop[nt][ks] = hv ? x : zero8();
+            }
+        }
+    };
+    auto post = [&]() {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bool hv = h_wave + nt * 16 + n < a.H;
+            // +inf for a saturating sink: every P is 0
+            lse2[nt] = hv ? (a.sink ? glae(l_raw[nt], sk_raw[nt]) : l_raw[nt]) * LOG2E : 0.f;
         }
     };
     float pdp[NT];
@@ -674,7 +693,7 @@ __global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
                                                                     gs);
                                  else
                                      gs.all();
-                             }, NoPre{}, post);
+                             }, NoPre{}, post, early);
     // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
