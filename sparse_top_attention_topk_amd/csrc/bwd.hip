@@ -1129,9 +1129,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     constexpr int RN = (DQK - DV) / 16;                 // rope column tiles (4 or 0)
     static_assert(RN <= NW, "one rope column tile per wave at most");
     constexpr int HP = 32 * HK;                         // heads padded
-    // four LDS buffers of one size: s_st0, s_st1 and s_pd1 take the staged
-    // q / dO pieces in turn (three in flight); afterwards s_pd0 / s_pd1 hold
-    // the [P | dS] tiles of even / odd blocks
+    // four LDS buffers of one size: all four take the staged q / dO pieces in
+    // turn (three in flight); afterwards s_pd1 / s_pd0 hold the [P | dS] tiles
+    // of even / odd blocks
     constexpr int SLOT = 32 * DQK > 2 * HP * BLK ? 32 * DQK : 2 * HP * BLK;
     __shared__ __attribute__((aligned(16))) __bf16 s_st0[SLOT];
     __shared__ __attribute__((aligned(16))) __bf16 s_st1[SLOT];
@@ -1157,57 +1157,64 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const bool has_rope = RW > 0 && wave < RN;           // uniform
     const int c_rope = DV + 16 * wave;
 
-    // heads past H: their P / dS tile rows stay zero (never loaded; s_pd1 is
-    // cleared after its turn as a staging buffer)
+    // heads past H: their P / dS tile rows stay zero (never loaded; s_pd0 and
+    // s_pd1 are cleared after their last turn as staging buffers)
     auto zero_rows_past_h = [&](__bf16* buf) {
         for (int i = a.H * BLK / 8 + tid; i < HP * BLK / 8; i += NW * 64) {
             reinterpret_cast<u32x4*>(buf)[i] = u32x4{0u, 0u, 0u, 0u};
             reinterpret_cast<u32x4*>(buf + HP * BLK)[i] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    if (HP > a.H) zero_rows_past_h(s_pd0);
 
     // ---- q and dO with heads in-lane: lane (g, n) of k-step hk, column tile
     // nt holds X[32hk + 8g + j][c + n], j = 0..7, c the tile's first column
     // (c_wave + 16 nt, or c_rope for the rope tile nt = MW).  Staged in 2*HK
     // pieces of 32 head rows (rows past H repeat row H-1: their P and dS are
-    // zero) through a ring of three buffers: piece p + 2 loads while piece p
-    // is read and piece p + 1 lands.  The [P | dS] tile of block 0 loads first
-    // (into s_pd0, outside the ring), so it is there when the pieces are.
+    // zero) through a ring of all four buffers: pieces p + 1 .. p + 3 load
+    // while piece p is read, about 110 KB in flight.  The [P | dS] tile of
+    // block 0 loads into s_pd1 as soon as the ring is done with it; the blocks
+    // then take s_pd1 (even) and s_pd0 (odd).
     bf16x8 qB[HK][MW + RW], dB[HK][MW];
     constexpr int NPC = 2 * HK;
-    __bf16* const ring[3] = {s_st0, s_st1, s_pd1};
+    constexpr int RING = 4;
+    // the last piece staged in s_pd1 (ring slot 2), -1 if none; never the
+    // last piece (NPC is even)
+    constexpr int LAST_PD1 = NPC > 2 ? ((NPC - 1 - 2) / RING) * RING + 2 : -1;
+    static_assert(NPC % 2 == 0 && LAST_PD1 < NPC - 1, "s_pd1 is free before the last piece");
+    __bf16* const ring[RING] = {s_st0, s_st1, s_pd1, s_pd0};
     auto issue = [&](int piece) {
         const int hk = piece >> 1;
         const int nv = a.H - 32 * hk;
         const size_t row0 = (size_t)t * a.H + 32 * hk;
-        if ((piece & 1) == 0) stage_rows_async<DQK, NW>(ring[piece % 3], a.q + row0 * DQK, nv, wave, lane);
-        else stage_rows_async<DV, NW>(ring[piece % 3], a.dO + row0 * DV, nv, wave, lane);
+        if ((piece & 1) == 0) stage_rows_async<DQK, NW>(ring[piece % RING], a.q + row0 * DQK, nv, wave, lane);
+        else stage_rows_async<DV, NW>(ring[piece % RING], a.dO + row0 * DV, nv, wave, lane);
+    };
+    auto first_tile = [&]() {
+        if (HP > a.H) zero_rows_past_h(s_pd1);
+        pd_tiles_async<HP, NW>(a, s_pd1, t, b_lo, wave, lane);
     };
     // each wave issues at least 4 loads per piece (d_qk or d_v columns x 32
-    // rows in 16-byte loads over 8 waves): waiting down to 4 outstanding
-    // loads completes every load issued before the last piece (loads complete
-    // in issue order)
+    // rows in 16-byte loads over 8 waves): with k pieces issued after piece p,
+    // waiting down to 4 k outstanding loads completes every load of piece p
+    // (loads complete in issue order)
     static_assert((32 * (DV / 8) / 64) / NW >= 4, "the ring waits assume at least 4 loads per piece");
-    __syncthreads();                      // zero-fill done before any tile load lands
-    pd_tiles_async<HP, NW>(a, s_pd0, t, b_lo, wave, lane);
     if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b_lo, lane);
-    issue(0);
-    if (NPC > 1) issue(1);
+    if (LAST_PD1 < 0) first_tile();
+#pragma unroll
+    for (int piece = 0; piece < RING - 1 && piece < NPC; ++piece) issue(piece);
 #pragma unroll
     for (int piece = 0; piece < NPC; ++piece) {
-        if (piece + 1 < NPC) {
-            // piece + 1 stays in flight.  A plain barrier: the workgroup fence
-            // of __syncthreads would wait for every outstanding LDS-bound
-            // load.  lgkmcnt(0): this wave's reads of piece - 1 are done
-            // before its buffer is reloaded.
-            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        } else {
-            wait_vmem();
-            __syncthreads();
-        }
-        if (piece + 2 < NPC) issue(piece + 2);            // into the buffer of piece - 1
-        const __bf16* cur = ring[piece % 3];
+        // pieces piece + 1, piece + 2 stay in flight.  A plain barrier: the
+        // workgroup fence of __syncthreads would wait for every outstanding
+        // LDS-bound load.  lgkmcnt(0): this wave's reads of piece - 1 are
+        // done before its buffer is reloaded.
+        const int after = NPC - 1 - piece < RING - 2 ? NPC - 1 - piece : RING - 2;
+        if (after == 2) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (after == 1) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (piece + RING - 1 < NPC) issue(piece + RING - 1);     // into the buffer of piece - 1
+        if (LAST_PD1 >= 0 && piece == LAST_PD1 + 1) first_tile();   // s_pd1's last piece is read
+        const __bf16* cur = ring[piece % RING];
         const int hk = piece >> 1;
         // operands are read unconditionally (column clamped into the piece)
         // and zeroed after: no branch around the LDS reads
@@ -1225,12 +1232,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
             qB[hk][MW + RW - 1] = has_rope ? x : zero8();
         }
     }
-    // Every wave must be done reading the last staged piece before s_pd1's
-    // padded rows are cleared: with HK = 3 that piece lives in s_pd1.  The
-    // block loop's first barrier then orders the clearing before the reads.
+    // s_pd0 (ring slot 3) is done after the last piece: every wave must have
+    // read it before its padded rows are cleared; the block loop's first
+    // barrier then orders the clearing before the reads.
     if (HP > a.H) {
         __syncthreads();
-        zero_rows_past_h(s_pd1);
+        zero_rows_past_h(s_pd0);
     }
 
     // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
@@ -1252,18 +1259,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         wait_vmem();
         __syncthreads();
         if (b + 1 < b_end) {
-            pd_tiles_async<HP, NW>(a, s_pd1, t, b + 1, wave, lane);
+            pd_tiles_async<HP, NW>(a, s_pd0, t, b + 1, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[1], a.idx, t, a.W, b + 1, lane);
         }
-        block(s_pd0, s_raw[0], b);
+        block(s_pd1, s_raw[0], b);
         if (b + 1 >= b_end) break;
         wait_vmem();
         __syncthreads();
         if (b + 2 < b_end) {
-            pd_tiles_async<HP, NW>(a, s_pd0, t, b + 2, wave, lane);
+            pd_tiles_async<HP, NW>(a, s_pd1, t, b + 2, wave, lane);
             if (wave == 0) stage_slot_idx(s_raw[0], a.idx, t, a.W, b + 2, lane);
         }
-        block(s_pd1, s_raw[1], b + 1);
+        block(s_pd0, s_raw[1], b + 1);
     }
 }
 
