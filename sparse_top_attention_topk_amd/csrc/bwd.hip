@@ -365,18 +365,10 @@ __device__ __forceinline__ int valid_row_b(int v, int j, int L, int S_kv) {
 }
 
 // The double-buffered gather loop of the kernels that gather KV tiles:
-// body(tile, rows, b, parity, gs, live) runs block b from tile 0 (even b,
-// parity 0) or tile 1 (odd b, parity 1) and issues, spread over its math
-// (GatherSpread), this wave's share of the gather of block b + 1 from the
-// slot rows grows into the other tile gtile (the last block issues none).
-// pre(b, parity)
-// runs before block b - 1's body and may issue global loads for block b
-// (they complete before block b starts, and waiting for them never waits for
-// a gather issued after them).
-struct NoPre {
-    template <typename P>
-    __device__ void operator()(int, P) const {}
-};
+// body(tile, rows, b, gs, live) runs block b from tile 0 (even b) or tile 1
+// (odd b) and issues, spread over its math (GatherSpread), this wave's share
+// of the gather of block b + 1 from the slot rows grows into the other tile
+// gtile (the last block issues none).
 
 // The next block's gather, one load per step of a matrix loop: main rows at
 // steps 0 .. RPW - 1, rope loads at the steps after (a 1 KB row load takes
@@ -424,15 +416,13 @@ __device__ __forceinline__ BlockRange block_range(const BwdArgs& a, int L) {
     return {b_lo, L < j_end ? L : j_end};
 }
 
-template <int DQK, int NW, typename Body, typename Pre = NoPre, typename Post = NoPost, typename Early = NoPost>
+template <int DQK, int NW, typename Body, typename Post = NoPost, typename Early = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
                                                 int (*s_rows)[BLK], int* s_live, int* s_last, int t, int L, int nblk,
-                                                BlockRange rg, int wave, int lane, Body&& body, Pre&& pre = Pre{},
-                                                Post&& post = Post{}, Early&& early = Early{}) {
+                                                BlockRange rg, int wave, int lane, Body&& body, Post&& post = Post{},
+                                                Early&& early = Early{}) {
     const int b_lo = rg.b_lo, j_hi = rg.j_hi;
     using Tile = KvTileSwz<DQK>;
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
     const auto kvr = Tile::kv_rsrc(a.kv, a.S_kv);
     const int tid = threadIdx.x;
     // The row's last valid slot: the blocks after its block hold padding only
@@ -483,10 +473,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
     const int nbr = nblk;                                   // blocks of the row
     nblk = __builtin_amdgcn_readfirstlane(last < 0 ? 0 : last / BLK + 1 - b_lo);   // blocks of the range
     if (nbr > 0) {
-        if (nblk > 0) {
-            pre(b_lo, P0{});
-            Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
-        }
+        if (nblk > 0) Tile::template gather_async<NW>(s_tile0, s_rows[0], kvr, wave, lane, a.S_kv);
         post();
     }
     // Block k: wait for its tile; store the slot rows of block k + 1 (their
@@ -503,8 +490,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b_lo + b + 2) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < nblk) pre(b_lo + b + 1, P1{});
-        body(s_tile0, s_rows[b % 3], b_lo + b, P0{},
+        body(s_tile0, s_rows[b % 3], b_lo + b,
              GatherSpread<DQK, NW>(s_tile1, s_rows[(b + 1) % 3], a.kv, wave, lane, a.S_kv, b + 1 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[b % 3]) != 0);
         if (b + 1 >= nblk) break;
@@ -515,8 +501,7 @@ __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile
         __syncthreads();
         ahead = tid < BLK ? raw_index_b(a, t, (b_lo + b + 3) * BLK + tid) : 0;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < nblk) pre(b_lo + b + 2, P0{});
-        body(s_tile1, s_rows[(b + 1) % 3], b_lo + b + 1, P1{},
+        body(s_tile1, s_rows[(b + 1) % 3], b_lo + b + 1,
              GatherSpread<DQK, NW>(s_tile0, s_rows[(b + 2) % 3], a.kv, wave, lane, a.S_kv, b + 2 < nblk),
              __builtin_amdgcn_readfirstlane(s_live[(b + 1) % 3]) != 0);
     }
@@ -687,13 +672,13 @@ __global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
     const typename Tile::Lane TL = Tile::lane_bases(lane);
     gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
                              wave, lane,
-                             [&](const __bf16* tile, const int* rows, int, auto, const auto& gs, bool live) {
+                             [&](const __bf16* tile, const int* rows, int, const auto& gs, bool live) {
                                  if (active && live)
                                      delta_exact_block<DQK, NW, NT>(a, tile, TL, rows, qop, dop, lse2, pdp, lane,
                                                                     gs);
                                  else
                                      gs.all();
-                             }, NoPre{}, post, early);
+                             }, post, early);
     // lanes (g, n), g = 0..3, hold slot subsets of head n: sum them
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -944,13 +929,13 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
         const typename Tile::Lane TL = Tile::lane_bases(lane);
         gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
                                  wave, lane,
-                                 [&](const __bf16* tile, const int* rows, int b, auto, const auto& gs, bool live) {
+                                 [&](const __bf16* tile, const int* rows, int b, const auto& gs, bool live) {
                                      if (active && live)
                                          sdq_block<DQK>(a, tile, TL, rows, qop, dop, lse2, dlt, acc, t, head, b,
                                                         lane, gs);
                                      else
                                          gs.all();
-                                 }, NoPre{}, post, early);
+                                 }, post, early);
     }
 
     if (!hv) return;
