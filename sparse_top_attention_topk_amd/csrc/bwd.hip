@@ -1060,6 +1060,32 @@ __device__ __forceinline__ bf16x8 pd_op(const __bf16* tile, int h0, int s0, int 
     return cat44(lds_tr4(tile + e0), lds_tr4(tile + e1));
 }
 
+// The four 8-byte blocks that lanes (g, n), g = 0..3, hold for one slot n
+// and column tile nt (columns c + 16 nt + 4 g .. +3), transposed over g: lane g
+// ends with tile g's 32 contiguous bytes (its four blocks in column order), so
+// a slot's 128 bytes go out as two 16-byte stores per lane instead of four
+// 8-byte ones.  Two swap steps between 16-lane rows: rows 2, 3 of tiles 0, 1
+// with rows 0, 1 of tiles 2, 3; then rows 1, 3 of tiles 0, 2 with rows 0, 2 of
+// tiles 1, 3.
+__device__ __forceinline__ void transpose_blocks(u32x2 (&r)[4]) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto x = __builtin_amdgcn_permlane32_swap(r[d][w], r[2 + d][w], false, false);
+            r[d][w] = x[0];
+            r[2 + d][w] = x[1];
+        }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto x = __builtin_amdgcn_permlane16_swap(r[2 * c][w], r[2 * c + 1][w], false, false);
+            r[2 * c][w] = x[0];
+            r[2 * c + 1][w] = x[1];
+        }
+}
+
 template <int DQK, int HK, int MW, int RW, bool ROPE>
 __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, const int* raw,
                                           const bf16x8 (&qB)[HK][MW + RW], const bf16x8 (&dB)[HK][MW], int b,
@@ -1091,15 +1117,22 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
             if constexpr (ROPE) acc[MW] = mfma16(qB[hk][MW], bds, acc[MW]);
         }
         // lane (g, n) holds columns c + 4g .. +3 of slot 16 qt + n for each of
-        // its column tiles, stored as one 4-value block (8 bytes); only valid
-        // slots are written (the row lists name no other slot)
+        // its column tiles, one 4-value block (8 bytes) each; the main tiles'
+        // blocks are transposed over g (all four lanes of a slot take part: a
+        // slot's validity is the same for them) and stored 16 bytes at a time.
+        // Only valid slots are written (the row lists name no other slot).
+        u32x2 blk[MW];
+#pragma unroll
+        for (int nt = 0; nt < MW; ++nt) blk[nt] = pack_blk4(acc[nt]);
+        transpose_blocks(blk);
         const int slot = 16 * qt + n;
         const int v = raw[slot];
         if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
             const int soff = (b * BLK + 16 * qt) * (2 * DQK);
-#pragma unroll
-            for (int nt = 0; nt < MW; ++nt)
-                __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[nt]), prs, voff + 32 * nt, soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{blk[0][0], blk[0][1], blk[1][0], blk[1][1]}, prs, voff,
+                                                   soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{blk[2][0], blk[2][1], blk[3][0], blk[3][1]}, prs,
+                                                   voff + 16, soff, 0);
             if constexpr (ROPE) __builtin_amdgcn_raw_buffer_store_b64(pack_blk4(acc[MW]), prs, voff_rope, soff, 0);
         }
     }
@@ -1227,11 +1260,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
     // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
-    // slot 16 qt + n, columns c + 4g .. +3 of each of its column tiles
+    // slot 16 qt + n, columns c_wave + 16g .. +15 (the main tiles, after the
+    // transpose) and c_rope + 4g .. +3 (its rope tile)
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
         0x00020000);
-    const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 4 * (lane >> 4));
+    static_assert(MW == 4, "the block transpose takes four main column tiles per wave");
+    const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 16 * (lane >> 4));
     const int voff_rope = (lane & 15) * (2 * DQK) + 2 * (c_rope + 4 * (lane >> 4));
     // one copy of the block per kind of wave, so the MFMAs stay in one basic block
     auto block = [&](const __bf16* pd, const int* raw, int b) __attribute__((always_inline)) {
@@ -1430,9 +1465,10 @@ static hipError_t launch_chunk_t(const BwdArgs& a, hipStream_t stream, const Mar
     mark(1);
     const int hk = (a.H + 31) / 32;
     const int ns = a.nsplit > 1 ? a.nsplit : 1;    // workgroups per token (block ranges)
-    // sdp: 16 heads per wave keep q and dO (the B operands) within half the
-    // register file, so two waves share each SIMD and hide each other's
-    // gather and LDS latency; 8 such waves cover 128 heads.
+    // S/dP and dQ: one workgroup per token and group of 64 heads (4 waves of
+    // 16, one per SIMD: q, dO and the dQ^T accumulators take most of the
+    // register file); a token's groups are numbered 8 apart, so they run on
+    // one XCD and the second finds the gathered rows in its L2.
     hipLaunchKernelGGL((bwd_sdq_kernel<DQK>), dim3((a.Tc + 7) / 8 * 8 * ((a.H + 63) / 64), 1, ns), dim3(256), 0,
                        stream, a);
     mark(2);
