@@ -715,6 +715,27 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(BwdArgs a) {
     }
 }
 
+// Two 8-byte pieces x0, x1 in each of the lanes (g, n), g = 0..3, of one row n:
+// piece m of lane g covers elements 16 m + 4 g .. +3 of a 32-element stretch.
+// Afterwards lane g holds elements 8 g .. 8 g + 7 (x0 the first four), so the
+// stretch goes out as one 16-byte store per lane.  Two swap steps between
+// 16-lane rows: rows 2, 3 of x0 with rows 0, 1 of x1, then rows 1, 3 of x0
+// with rows 0, 2 of x1.
+__device__ __forceinline__ void transpose_pairs(u32x2& x0, u32x2& x1) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const auto x = __builtin_amdgcn_permlane32_swap(x0[w], x1[w], false, false);
+        x0[w] = x[0];
+        x1[w] = x[1];
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const auto x = __builtin_amdgcn_permlane16_swap(x0[w], x1[w], false, false);
+        x0[w] = x[0];
+        x1[w] = x[1];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bwd_sdq: S, P, dP, dS and dQ of 64 heads of one token in one pass over the
 // token's gathered blocks.  Four waves of 16 heads, one per SIMD: q and dO
@@ -797,17 +818,22 @@ __device__ __forceinline__ void sdq_block(const BwdArgs& a, const __bf16* tile,
 
     // bf16 P and dS' of half h: stored for the dKV pass; dS' returned as the B
     // operand of dQ^T (lane (g, n) holds slots 32 h + 4g + j and
-    // 32 h + 16 + 4g + j of head n, the order of slot_op)
+    // 32 h + 16 + 4g + j of head n, the order of slot_op).  For the stores the
+    // pieces are regrouped over g (transpose_pairs): lane (g, n) writes slots
+    // 32 h + 8g .. +7 of head n, 16 bytes, into P and into dS'.
     auto finish = [&](auto H) {
         constexpr int h = decltype(H)::value;
         const bf16x4 ds_lo = cvt4(dpacc[h][0][0], dpacc[h][0][1], dpacc[h][0][2], dpacc[h][0][3]);
         const bf16x4 ds_hi = cvt4(dpacc[h][1][0], dpacc[h][1][1], dpacc[h][1][2], dpacc[h][1][3]);
+        u32x2 p0 = __builtin_bit_cast(u32x2, cvt4(sacc[h][0][0], sacc[h][0][1], sacc[h][0][2], sacc[h][0][3]));
+        u32x2 p1 = __builtin_bit_cast(u32x2, cvt4(sacc[h][1][0], sacc[h][1][1], sacc[h][1][2], sacc[h][1][3]));
+        u32x2 d0 = __builtin_bit_cast(u32x2, ds_lo), d1 = __builtin_bit_cast(u32x2, ds_hi);
+        transpose_pairs(p0, p1);
+        transpose_pairs(d0, d1);
         if (hv) {
-            const size_t base = ((size_t)(t - a.t0) * a.H + head) * a.Wp + b * BLK + h * 32 + 4 * g;
-            st4(a.ws_p + base, cvt4(sacc[h][0][0], sacc[h][0][1], sacc[h][0][2], sacc[h][0][3]));
-            st4(a.ws_p + base + 16, cvt4(sacc[h][1][0], sacc[h][1][1], sacc[h][1][2], sacc[h][1][3]));
-            st4(a.ws_ds + base, ds_lo);
-            st4(a.ws_ds + base + 16, ds_hi);
+            const size_t base = ((size_t)(t - a.t0) * a.H + head) * a.Wp + b * BLK + h * 32 + 8 * g;
+            *reinterpret_cast<u32x4*>(a.ws_p + base) = u32x4{p0[0], p0[1], p1[0], p1[1]};
+            *reinterpret_cast<u32x4*>(a.ws_ds + base) = u32x4{d0[0], d0[1], d1[0], d1[1]};
         }
         return cat44(ds_lo, ds_hi);
     };
@@ -946,9 +972,18 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
         for (int mc = 0; mc < MC; ++mc) *reinterpret_cast<f32x4*>(dp + 16 * mc) = acc[mc];
         return;
     }
-    __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 4 * g;
+    // bf16 dQ: column tiles in pairs, regrouped over g (transpose_pairs) so
+    // that lane (g, n) writes columns 32 k + 8 g .. +7 of head n, 16 bytes
+    static_assert(MC % 2 == 0, "dQ column tiles go out in pairs");
+    __bf16* dqp = a.dq + ((size_t)t * a.H + head) * DQK + 8 * g;
 #pragma unroll
-    for (int mc = 0; mc < MC; ++mc) st4(dqp + 16 * mc, cvt4(acc[mc][0], acc[mc][1], acc[mc][2], acc[mc][3]));
+    for (int k = 0; k < MC / 2; ++k) {
+        const f32x4 lo = acc[2 * k], hi = acc[2 * k + 1];
+        u32x2 x0 = __builtin_bit_cast(u32x2, cvt4(lo[0], lo[1], lo[2], lo[3]));
+        u32x2 x1 = __builtin_bit_cast(u32x2, cvt4(hi[0], hi[1], hi[2], hi[3]));
+        transpose_pairs(x0, x1);
+        *reinterpret_cast<u32x4*>(dqp + 32 * k) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+    }
 }
 
 // ---------------------------------------------------------------------------
