@@ -130,42 +130,42 @@ __device__ __forceinline__ void put_rows(int* rows, int* live, int r, int lane) 
 }
 
 // Block storage of fp32 values in 16 bits each (the dKV partials): a group of
-// four values keeps the largest fp32 exponent field E among them (8 bits) and
-// each value as a 14-bit signed multiple of 2^(E - 139), i.e. of 2^-12 times
-// the group's leading power of two.  A value's error is at most 2^-13 of the
-// group's largest magnitude (2^-12 where rounding reaches the end of the
-// range).  Groups below 2^-114 are stored as zero; a group holding a
-// non-finite value decodes as NaN.  Layout: w0 = E | q0 << 8 | (q1 & 0x3FF)
-// << 22, w1 = q1 >> 10 | q2 << 4 | q3 << 18 (q in 14-bit two's complement).
+// four values keeps E = max(13, the largest fp32 exponent field among them)
+// (8 bits) and each value as a 14-bit signed multiple of 2^(E - 139), i.e. of
+// 2^-12 times the group's leading power of two.  A value's error is at most
+// 2^-13 of the group's largest magnitude (2^-12 where rounding reaches the
+// end of the range); groups below 2^-114 are kept to 2^-127 absolute.  A group
+// holding a non-finite value has E = 255 and decodes as NaN.  Layout:
+// w0 = E | q0 << 8 | (q1 & 0x3FF) << 22, w1 = q1 >> 10 | q2 << 4 | q3 << 18
+// (q in 14-bit two's complement).
 __device__ __forceinline__ u32x2 pack_blk4(f32x4 v) {
-    // E: the largest exponent field, i.e. that of the largest magnitude bits
-    // (through scalars: a bit cast of a vector element can read the wrong
-    // element with this compiler)
-    uint32_t b[4];
+    // E from the exponent fields (through scalars: a bit cast of a vector
+    // element can read the wrong element with this compiler)
+    float x[4];
+    uint32_t e4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float x = v[i];
-        b[i] = __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu;
+        x[i] = v[i];
+        e4[i] = __builtin_amdgcn_ubfe(__builtin_bit_cast(uint32_t, x[i]), 23, 8);
     }
-    const uint32_t bm01 = b[0] > b[1] ? b[0] : b[1];
-    const uint32_t bm23 = b[2] > b[3] ? b[2] : b[3];
-    const uint32_t e = (bm01 > bm23 ? bm01 : bm23) >> 23;
-    const float sc = __builtin_bit_cast(float, (266u - (e > 12u ? e : 13u)) << 23);   // 2^(139 - E)
-    uint32_t q[4];
+    const uint32_t e01 = e4[0] > e4[1] ? e4[0] : e4[1];
+    const uint32_t e23 = e4[2] > e4[3] ? e4[2] : e4[3];
+    uint32_t e = e01 > e23 ? e01 : e23;
+    e = e > 13u ? e : 13u;
+    const float sc = __builtin_bit_cast(float, (266u - e) << 23);   // 2^(139 - E), a normal number
+    // |x sc| < 2^13: adding 1.5 * 2^23 in one rounding leaves round-to-
+    // nearest-even(x sc) in the low bits, as rint(x sc) would; the result,
+    // clamped to +-8191 (a float median: r is an integer plus 1.5 * 2^23),
+    // holds q in two's complement in its low 14 bits
+    uint32_t u[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // |v sc| < 2^13: adding 1.5 * 2^23 in one rounding leaves round-to-
-        // nearest-even(v sc) in the low bits, as rint(v sc) would
-        const float r = __builtin_fmaf(v[i], sc, 12582912.0f);
-        int qi = (int)(__builtin_bit_cast(uint32_t, r) - 0x4B400000u);
-        qi = qi < -8191 ? -8191 : (qi > 8191 ? 8191 : qi);
-        q[i] = (uint32_t)qi & 0x3FFFu;
+        const float r = __builtin_fmaf(x[i], sc, 12582912.0f);
+        u[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_fmed3f(r, 12582912.0f - 8191.0f, 12582912.0f + 8191.0f));
     }
-    const uint32_t w0 = e | (q[0] << 8) | (q[1] << 22);
-    const uint32_t w1 = (q[1] >> 10) | (q[2] << 4) | (q[3] << 18);
-    // selects, not a branch: small blocks store 0, non-finite ones {255, 0}
-    const bool keep = e > 12u, inf = e == 255u;
-    return u32x2{inf ? 255u : (keep ? w0 : 0u), keep && !inf ? w1 : 0u};
+    const uint32_t w0 = e | ((u[0] << 8) & 0x3FFF00u) | (u[1] << 22);
+    const uint32_t w1 = ((u[1] >> 10) & 0xFu) | ((u[2] << 4) & 0x3FFF0u) | (u[3] << 18);
+    return u32x2{w0, w1};
 }
 
 __device__ __forceinline__ f32x4 unpack_blk4(u32x2 w) {
