@@ -1397,7 +1397,25 @@ __global__ __launch_bounds__(256) void dkv_combine_kernel(BwdArgs a) {
     f32x4 acc[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = zero4();
-    for (int p = p0; p < p1; ++p) {
+    // four parts' loads in flight, summed in part order (the first rows have
+    // tens of parts: a load round trip per part would set the kernel's time)
+    constexpr int UP = 4;
+    int p = p0;
+    for (; p + UP <= p1; p += UP) {
+        f32x4 x[UP][NV];
+#pragma unroll
+        for (int k = 0; k < UP; ++k)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int c = 4 * (lane + 64 * v);
+                x[k][v] = c < DQK ? *reinterpret_cast<const f32x4*>(a.part_sum + (size_t)(p + k) * DQK + c) : zero4();
+            }
+#pragma unroll
+        for (int k = 0; k < UP; ++k)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) acc[v] += x[k][v];
+    }
+    for (; p < p1; ++p) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int c = 4 * (lane + 64 * v);
@@ -1426,14 +1444,26 @@ __global__ __launch_bounds__(256) void dsink_kernel(const float* __restrict__ ls
     const int h = blockIdx.x;
     const float sk = sink[h];
     float acc = 0.f;
-    for (int t = threadIdx.x; t < T; t += 256) {
-        const float l = lse[(size_t)t * H + h];
-        if (l == -INFINITY) continue;
-        float ps;
-        if (sk == -INFINITY) ps = 0.f;
-        else if (sk == INFINITY && l == INFINITY) ps = 0.5f;
-        else ps = sigmoid(sk - l);
-        acc += ps * delta[(size_t)t * H + h];
+    // U tokens per thread in flight (the loads of a head are H floats apart,
+    // one 64-byte segment each: latency, not bandwidth, sets the time)
+    constexpr int U = 8;
+    for (int t0 = threadIdx.x; t0 < T; t0 += 256 * U) {
+        float l[U], d[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 256 * u;
+            l[u] = t < T ? lse[(size_t)t * H + h] : -INFINITY;
+            d[u] = t < T ? delta[(size_t)t * H + h] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (l[u] == -INFINITY) continue;
+            float ps;
+            if (sk == -INFINITY) ps = 0.f;
+            else if (sk == INFINITY && l[u] == INFINITY) ps = 0.5f;
+            else ps = sigmoid(sk - l[u]);
+            acc += ps * d[u];
+        }
     }
     s_part[threadIdx.x] = acc;
     __syncthreads();
