@@ -106,17 +106,45 @@ struct InvPart {
     }
 };
 
+// The row of local slot i of a sub-chunk's token-major slot range (tokens
+// t_begin ..), relative to r0, or -1 when the slot is not valid.  The index
+// load is unconditional (i clamped into the range), so that several can be
+// in flight.
+// Branch-free row_length: the length load always happens (from the index
+// array when there are no lengths), so a wait placed for one load does not
+// cover the others in flight.
+__device__ __forceinline__ int row_length_nb(const BwdArgs& a, int t) {
+    const int32_t* p = a.len != nullptr ? a.len + t : a.idx;
+    const int v = *p;
+    const int L = v < 0 ? 0 : (v > a.W ? a.W : v);
+    return a.len != nullptr ? L : a.W;
+}
+
+__device__ __forceinline__ int flat_slot_row(const BwdArgs& a, const InvPart& P, int i, int n) {
+    const int ic = i < n ? i : n - 1;
+    const int tl = ic / a.W;
+    const int t = P.t_begin + tl, j = ic - tl * a.W;
+    const int v = a.idx[(size_t)t * a.W + j];
+    const int L = row_length_nb(a, t);
+    return (i < n && j < L && v >= 0 && v < a.S_kv) ? v - P.r0 : -1;
+}
+
 __global__ __launch_bounds__(256) void rows_count_kernel(BwdArgs a) {
     extern __shared__ int s_cnt[];           // [nr]
     const InvPart P(a);
     for (int i = threadIdx.x; i < P.nr; i += 256) s_cnt[i] = 0;
     __syncthreads();
-    for (int t = P.t_begin; t < P.t_end; ++t) {
-        const int L = row_length(a.len, t, a.W);
-        for (int j = threadIdx.x; j < L; j += 256) {
-            const int r = slot_row(a.idx, t, a.W, L, a.S_kv, j) - P.r0;
-            if ((unsigned)r < (unsigned)P.nr) atomicAdd(s_cnt + r, 1);
-        }
+    // the sub-chunk's slots as one range, U index loads in flight per thread
+    // (counting does not depend on the order)
+    constexpr int U = 8;
+    const int n = (P.t_end - P.t_begin) * a.W;
+    for (int i0 = threadIdx.x; i0 < n; i0 += 256 * U) {
+        int r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = flat_slot_row(a, P, i0 + 256 * u, n);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if ((unsigned)r[u] < (unsigned)P.nr) atomicAdd(s_cnt + r[u], 1);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < P.nr; i += 256)
@@ -135,19 +163,31 @@ __global__ __launch_bounds__(256) void rows_chunkscan_kernel(BwdArgs a) {
     const int per = (nch + 7) / 8;
     const int c0 = part * per < nch ? part * per : nch;
     const int c1 = c0 + per < nch ? c0 + per : nch;
+    // U counts in flight per thread in both passes
+    constexpr int U = 8;
     int sum = 0;
     if (r < a.S_kv)
-        for (int c = c0; c < c1; ++c) sum += a.chunk_cnt[(size_t)c * a.S_kv + r];
+        for (int c = c0; c < c1; c += U) {
+            int v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = c + u < c1 ? a.chunk_cnt[(size_t)(c + u) * a.S_kv + r] : 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += v[u];
+        }
     s_sum[part][rl] = sum;
     __syncthreads();
     int run = 0;
     for (int q = 0; q < part; ++q) run += s_sum[q][rl];
     if (r >= a.S_kv) return;
-    for (int c = c0; c < c1; ++c) {
-        int* p = a.chunk_cnt + (size_t)c * a.S_kv + r;
-        const int v = *p;
-        *p = run;
-        run += v;
+    for (int c = c0; c < c1; c += U) {
+        int v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = c + u < c1 ? a.chunk_cnt[(size_t)(c + u) * a.S_kv + r] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c + u < c1) a.chunk_cnt[(size_t)(c + u) * a.S_kv + r] = run;
+            run += v[u];
+        }
     }
     if (part == 7) a.row_cnt[r] = run;
 }
@@ -335,8 +375,10 @@ __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
             int v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
+                // unconditional loads (index clamped): all 16 in flight
                 const int i = i0 + k * 256 + (int)threadIdx.x;
-                v[k] = i < P.nr ? ro[i] + cc[i] : 0;
+                const int ic = i < P.nr ? i : P.nr - 1;
+                v[k] = ro[ic] + cc[ic];
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -346,6 +388,51 @@ __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    constexpr int NJ = 4;
+    if (a.W <= NJ * 256) {
+        // a token's slots in registers (slot k * 256 + tid), the next token's
+        // indices loaded while the current token is placed; the barrier
+        // between tokens waits for the LDS cursors only
+        // raw indices and length of a token (validity is decided at use), in
+        // two register sets taken in turn: the next token's loads stay in
+        // flight while the current one is placed
+        // (the length is loaded through a lane-dependent address, so that the
+        // compiler does not move it to a scalar register at once, which would
+        // wait for the load right where it is issued)
+        int lane_zero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
+        auto load_token = [&](int t, int (&v)[NJ], int& len_raw) {
+            len_raw = *(a.len != nullptr ? a.len + t + lane_zero : a.idx + lane_zero);
+#pragma unroll
+            for (int k = 0; k < NJ; ++k) {
+                const int j = k * 256 + (int)threadIdx.x;
+                v[k] = a.idx[(size_t)t * a.W + (j < a.W ? j : a.W - 1)];
+            }
+        };
+        auto place = [&](int t, const int (&v)[NJ], int len_raw) {
+            const int L = a.len != nullptr ? (len_raw < 0 ? 0 : (len_raw > a.W ? a.W : len_raw)) : a.W;
+#pragma unroll
+            for (int k = 0; k < NJ; ++k) {
+                const int j = k * 256 + (int)threadIdx.x;
+                const int r = (j < L && v[k] >= 0 && v[k] < a.S_kv) ? v[k] - P.r0 : -1;
+                if ((unsigned)r < (unsigned)P.nr) a.entries[atomicAdd(s_cur + r, 1)] = (t - a.t0) * a.Wp + j;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // token order within the sub-chunk
+        };
+        // (the loads are not under a branch: past the sub-chunk's last token
+        // they reload it, unused)
+        const int t_last = P.t_end - 1;
+        int va[NJ], vb[NJ], la, lb;
+        load_token(P.t_begin, va, la);
+        for (int t = P.t_begin; t < P.t_end; t += 2) {
+            load_token(t + 1 < t_last ? t + 1 : t_last, vb, lb);
+            place(t, va, la);
+            if (t + 1 >= P.t_end) break;
+            load_token(t + 2 < t_last ? t + 2 : t_last, va, la);
+            place(t + 1, vb, lb);
+        }
+        return;
+    }
     for (int t = P.t_begin; t < P.t_end; ++t) {
         const int L = row_length(a.len, t, a.W);
         for (int j = threadIdx.x; j < L; j += 256) {
