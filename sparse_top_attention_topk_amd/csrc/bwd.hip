@@ -365,6 +365,48 @@ __global__ __launch_bounds__(256) void rows_parts_kernel(BwdArgs a) {
     for (int p = a.part_off[r]; p < a.part_off[r + 1]; ++p) a.part_row[p] = r;
 }
 
+// rows_fill's token loop for W <= 256 NJ: a token's slots in registers
+// (slot k * 256 + tid), raw indices and length in two register sets taken in
+// turn, so that the next token's loads stay in flight while the current one
+// is placed (validity is decided at use); the barrier between tokens waits
+// for the LDS cursors only.  The loads are not under a branch (past the
+// sub-chunk's last token they reload it, unused), and the length goes
+// through a lane-dependent address: moved to a scalar register at once, it
+// would be waited for right where it is issued.
+template <int NJ>
+__device__ __forceinline__ void fill_tokens(const BwdArgs& a, const InvPart& P, int* s_cur) {
+    int lane_zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
+    auto load_token = [&](int t, int (&v)[NJ], int& len_raw) {
+        len_raw = *(a.len != nullptr ? a.len + t + lane_zero : a.idx + lane_zero);
+#pragma unroll
+        for (int k = 0; k < NJ; ++k) {
+            const int j = k * 256 + (int)threadIdx.x;
+            v[k] = a.idx[(size_t)t * a.W + (j < a.W ? j : a.W - 1)];
+        }
+    };
+    auto place = [&](int t, const int (&v)[NJ], int len_raw) {
+        const int L = a.len != nullptr ? (len_raw < 0 ? 0 : (len_raw > a.W ? a.W : len_raw)) : a.W;
+#pragma unroll
+        for (int k = 0; k < NJ; ++k) {
+            const int j = k * 256 + (int)threadIdx.x;
+            const int r = (j < L && v[k] >= 0 && v[k] < a.S_kv) ? v[k] - P.r0 : -1;
+            if ((unsigned)r < (unsigned)P.nr) a.entries[atomicAdd(s_cur + r, 1)] = (t - a.t0) * a.Wp + j;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // token order within the sub-chunk
+    };
+    const int t_last = P.t_end - 1;
+    int va[NJ], vb[NJ], la, lb;
+    load_token(P.t_begin, va, la);
+    for (int t = P.t_begin; t < P.t_end; t += 2) {
+        load_token(t + 1 < t_last ? t + 1 : t_last, vb, lb);
+        place(t, va, la);
+        if (t + 1 >= P.t_end) break;
+        load_token(t + 2 < t_last ? t + 2 : t_last, va, la);
+        place(t + 1, vb, lb);
+    }
+}
+
 __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
     extern __shared__ int s_cur[];           // [nr]
     const InvPart P(a);
@@ -388,49 +430,12 @@ __global__ __launch_bounds__(256) void rows_fill_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    constexpr int NJ = 4;
-    if (a.W <= NJ * 256) {
-        // a token's slots in registers (slot k * 256 + tid), the next token's
-        // indices loaded while the current token is placed; the barrier
-        // between tokens waits for the LDS cursors only
-        // raw indices and length of a token (validity is decided at use), in
-        // two register sets taken in turn: the next token's loads stay in
-        // flight while the current one is placed
-        // (the length is loaded through a lane-dependent address, so that the
-        // compiler does not move it to a scalar register at once, which would
-        // wait for the load right where it is issued)
-        int lane_zero;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(lane_zero));
-        auto load_token = [&](int t, int (&v)[NJ], int& len_raw) {
-            len_raw = *(a.len != nullptr ? a.len + t + lane_zero : a.idx + lane_zero);
-#pragma unroll
-            for (int k = 0; k < NJ; ++k) {
-                const int j = k * 256 + (int)threadIdx.x;
-                v[k] = a.idx[(size_t)t * a.W + (j < a.W ? j : a.W - 1)];
-            }
-        };
-        auto place = [&](int t, const int (&v)[NJ], int len_raw) {
-            const int L = a.len != nullptr ? (len_raw < 0 ? 0 : (len_raw > a.W ? a.W : len_raw)) : a.W;
-#pragma unroll
-            for (int k = 0; k < NJ; ++k) {
-                const int j = k * 256 + (int)threadIdx.x;
-                const int r = (j < L && v[k] >= 0 && v[k] < a.S_kv) ? v[k] - P.r0 : -1;
-                if ((unsigned)r < (unsigned)P.nr) a.entries[atomicAdd(s_cur + r, 1)] = (t - a.t0) * a.Wp + j;
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // token order within the sub-chunk
-        };
-        // (the loads are not under a branch: past the sub-chunk's last token
-        // they reload it, unused)
-        const int t_last = P.t_end - 1;
-        int va[NJ], vb[NJ], la, lb;
-        load_token(P.t_begin, va, la);
-        for (int t = P.t_begin; t < P.t_end; t += 2) {
-            load_token(t + 1 < t_last ? t + 1 : t_last, vb, lb);
-            place(t, va, la);
-            if (t + 1 >= P.t_end) break;
-            load_token(t + 2 < t_last ? t + 2 : t_last, va, la);
-            place(t + 1, vb, lb);
-        }
+    if (a.W <= 4 * 256) {
+        fill_tokens<4>(a, P, s_cur);
+        return;
+    }
+    if (a.W <= 8 * 256) {
+        fill_tokens<8>(a, P, s_cur);
         return;
     }
     for (int t = P.t_begin; t < P.t_end; ++t) {
