@@ -337,6 +337,18 @@ def test_deep_row_lists(T):
     assert not errors, f"deep rows T={T}: " + "; ".join(errors)
 
 
+@pytest.mark.parametrize("T,W", ((40, 2600), (8, 5000)))
+def test_wide_rows(T, W):
+    """Rows wider than 2048 slots (the index inversion's fill walks a token's
+    slots in a loop instead of holding them in registers) and, with few
+    tokens, wider than the one-workgroup inversion takes (4096 slots): a
+    non-compact layout much wider than S_kv, against the oracle."""
+    p = wl.make_edge_wide(8, seed=150 + T, T=T, S=512, W=W)
+    say(f"[gpu] wide rows T={T} W={W}: S_kv={p.S_kv} H={p.H}")
+    errors = compare_full(run_gpu(p, DEV), run_oracle(p))
+    assert not errors, f"wide rows T={T} W={W}: " + "; ".join(errors)
+
+
 def test_batched_large_kv_set():
     """Three sequences whose concatenated KV set (43000 rows) is larger than
     one workgroup's inversion counters cover (32768 rows): O, LSE, dQ and
