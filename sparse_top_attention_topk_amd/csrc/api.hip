@@ -106,10 +106,11 @@ WsLayout ws_layout(const smla_dims* d, int C) {
 
 // ---- split forward: how many splits over each token's slot blocks.  A
 // token takes one workgroup per head tile; with few tokens the GPU's 256
-// CUs are not filled, so the blocks are split until one round of about 256
-// workgroups (one per CU) is filled, at most one split per block: a second
-// round costs more than the longer ranges, and every split adds its fp32
-// partial O to write and merge.
+// CUs are not filled, so the split forward runs head tiles of 64 (more
+// workgroups, each writing half the partial O of a 128-head tile) and splits
+// the blocks until one round of about 256 workgroups (one per CU) is filled,
+// at most one split per block: a second round costs more than the longer
+// ranges, and every split adds its fp32 partial O to write and merge.
 struct FwdSplit {
     int nsplit, bps, nb;
 };
@@ -118,7 +119,11 @@ FwdSplit fwd_split_for(const smla_dims* d) {
     const int64_t nb = ((int64_t)d->W + smla::BLK - 1) / smla::BLK;
     const int ht = smla::fwd_head_tile(d->H);
     const int64_t wgs = (int64_t)d->T * ((d->H + ht - 1) / ht);
-    int64_t s = wgs >= 128 ? 1 : 256 / wgs;
+    if (wgs >= 128) return {1, (int)nb, (int)nb};
+    // split: tiles of 64 heads (twice the workgroups at H > 64, each with
+    // half the partial O to write)
+    const int64_t wgs_split = (int64_t)d->T * ((d->H + smla::FWD_SPLIT_HEAD_TILE - 1) / smla::FWD_SPLIT_HEAD_TILE);
+    int64_t s = 256 / wgs_split;
     if (s > nb) s = nb;
     if (s > 64) s = 64;                          // the merge keeps one split per lane
     if (s < 2) return {1, (int)nb, (int)nb};

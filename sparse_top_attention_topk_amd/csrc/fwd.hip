@@ -547,8 +547,10 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream) {
-    // head tile: 4 waves x 32 heads (H > 64) or 4 waves x 16 heads
-    const bool wide = a.H > 64;
+    // head tile: 4 waves x 32 heads (H > 64) or 4 waves x 16 heads; with
+    // split KV always 16 heads per wave (FWD_SPLIT_HEAD_TILE)
+    static_assert(FWD_SPLIT_HEAD_TILE == 64, "the split forward runs 4 waves x 16 heads");
+    const bool wide = a.H > 64 && a.nsplit <= 1;
     if (d_qk == 576)
         return wide ? launch_fwd_t<576, 4, 2>(a, stream) : launch_fwd_t<576, 4, 1>(a, stream);
     return wide ? launch_fwd_t<512, 4, 2>(a, stream) : launch_fwd_t<512, 4, 1>(a, stream);

@@ -69,6 +69,8 @@ constexpr int INV_ROWS = 32768;
 hipError_t launch_fwd(int d_qk, const FwdArgs& a, hipStream_t stream);
 // head tile of the forward (heads per workgroup)
 inline int fwd_head_tile(int H) { return H > 64 ? 128 : 64; }
+// head tile of the forward with split KV (few tokens)
+constexpr int FWD_SPLIT_HEAD_TILE = 64;
 hipError_t launch_preprocess(const __bf16* o, const __bf16* dO, float* delta, int rows,
                              hipStream_t stream);
 // Delta[t, h] = sum_j P_j dP_j (uses q, kv, dO, lse, idx, len, sink, delta_out)

@@ -231,11 +231,12 @@ def test_chunk_choice_always_fits_its_workspace(shape):
 
 def test_forward_split_count():
     """The split forward splits only when the tokens give fewer than 128
-    workgroups, fills about one round of 256, never exceeds one split per
-    block nor 64 splits (the merge keeps one per lane)."""
+    workgroups (of up to 128 heads), then runs tiles of 64 heads and splits
+    until about one round of 256 workgroups is filled, never more than one
+    split per block nor 64 splits (the merge keeps one per lane)."""
     from sparse_top_attention_topk_amd import _lib
-    for T, H, W, want in [(4096, 128, 640, 0), (128, 128, 1152, 0), (1, 128, 1152, 18), (64, 128, 1152, 4),
-                          (16, 128, 1152, 16), (1, 8, 64, 0), (1, 128, 1 << 16, 64), (5, 24, 2176, 34)]:
+    for T, H, W, want in [(4096, 128, 640, 0), (128, 128, 1152, 0), (1, 128, 1152, 18), (64, 128, 1152, 2),
+                          (16, 128, 1152, 8), (1, 8, 64, 0), (1, 128, 1 << 16, 64), (5, 24, 2176, 34)]:
         nb = -(-W // 64)
         ws = _lib.smla_fwd_splitkv_workspace_size(T, 16384, H, 576, 512, W)
         if want == 0:

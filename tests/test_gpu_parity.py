@@ -396,7 +396,7 @@ SPLIT_CASES = {
     "decode-T64": lambda: wl.make_problem("decode_T64"),
     "decode-T16-h64-d512": lambda: wl.make_decode(16, H=64, d_qk=512, seed=140),
     "decode-T5-h24-k2048": lambda: wl.make_decode(5, S_kv=8192, H=24, topk=2048, seed=141),
-    "spiky-T96-h96": lambda: wl.make_spiky(96, T=96, window=32, topk=160, frac=0.5),
+    "spiky-T96-h64": lambda: wl.make_spiky(64, T=96, window=32, topk=160, frac=0.5),
     "decode-T1-k8064": lambda: wl.make_decode(1, H=128, topk=8064, seed=142),   # 128 blocks: 64 splits
     "edge-wide-h128-T64": lambda: wl.make_edge_wide(128, T=64),
 }
