@@ -21,7 +21,7 @@ from sparse_top_attention_topk_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-SEEDS = range(64)
+SEEDS = range(128)
 
 
 @pytest.mark.parametrize("seed", SEEDS)
