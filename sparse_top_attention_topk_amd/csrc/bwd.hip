@@ -980,16 +980,12 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
     // workgroup x -> (token, head group): the head groups of a token are 8
     // workgroups apart, so that they run on one XCD (workgroups go to the 8
     // XCDs in turn) at about the same time and the second gathers its rows
-    // from that XCD's L2.  Tokens in ascending order: the dKV pass takes
-    // them in descending order, so it starts on the tokens whose P, dS, q
-    // and dO this pass touched last, while they are still in the last-level
-    // cache (measured: both passes ~1.5 % faster at H = 128 than with the
-    // same order in both)
+    // from that XCD's L2; tokens the chunk's longest rows first
     const int ngrp = (a.H + HT - 1) / HT;
     const int blk = (int)blockIdx.x / (8 * ngrp), rem = (int)blockIdx.x % (8 * ngrp);
     const int ti = blk * 8 + rem % 8;
     if (ti >= a.Tc) return;                            // uniform: past the chunk's tokens
-    const int t = a.t0 + ti;
+    const int t = a.t0 + a.Tc - 1 - ti;
     const int h_wave = (rem / 8) * HT + wave * 16;
     const int head = h_wave + n;
     const bool hv = head < a.H;
@@ -1291,9 +1287,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // the chunk's tokens in descending order (the S/dP-dQ pass runs them in
-    // ascending order, so the first tokens here are the ones it touched last)
-    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;
+    const int t = a.t0 + a.Tc - 1 - (int)blockIdx.x;     // the chunk's longest rows first
     const int L = row_length(a.len, t, a.W);
     // the row's blocks [b_lo, b_end) (all of them without a split)
     const int nblk = (L + BLK - 1) / BLK;
