@@ -34,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -316,12 +317,27 @@ def stage_work(p, n):
     }
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def _strip_comments(text):
+    """C/C++ source without comments, trailing blanks and empty lines (string
+    and character literals kept as written)."""
+    text = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_hash():
+    """sha256 over the kernel sources' code: comments and layout do not count,
+    so that an edit of the documentation keeps a profile taken on the same code
+    valid, while any change to the code voids it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_top_attention_topk_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        if not f.endswith((".hip", ".h", ".cpp")):
+            continue
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -11,10 +11,12 @@
 //   d_sink  = -sum_t sigmoid(sink - lse) * Delta
 //
 // Kernels, in launch order (preprocess is its own entry point):
-//   rows_count / rows_chunkscan / rows_scan / rows_fill
+//   rows_count / rows_chunkscan / rows_scan / rows_parts / rows_fill
 //                invert the index lists: every valid (token, slot) is listed
 //                under its KV row, in token order (row r owns the segment
-//                [off[r], off[r+1]) of the list)
+//                [off[r], off[r+1]) of the list, cut into parts of at most 64
+//                entries); chunks of at most 16 tokens take rows_small, one
+//                workgroup doing all of it
 //   bwd_sdq      one workgroup per token and 64 heads: gathers each 64-slot
 //                KV tile (async, double-buffered), recomputes S, P, dP, dS
 //                with bf16 MFMA, stores P and scale*dS (bf16) to the workspace
