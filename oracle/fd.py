@@ -8,8 +8,6 @@ inner product of that direction with (dQ, dKV, d_sink).
 """
 from __future__ import annotations
 
-import numpy as np
-
 from .smla import oracle_fwd
 
 __all__ = ["loss", "directional_fd"]

@@ -2,7 +2,6 @@
 graph through the C ABI and replayed: every replay, with eager work on the
 outputs between replays, reproduces the eager step bit for bit (the library
 enqueues kernels only, no memsets, and its results are deterministic)."""
-import numpy as np
 import pytest
 import torch
 

@@ -8,7 +8,6 @@ bits; dKV sums each row chunk by chunk and dQ sums block ranges when a chunk
 has fewer than 128 tokens, so with a chunk size other than smla_bwd's they
 may differ by the summation grouping only (and must be the same bits when
 both run one chunk)."""
-import numpy as np
 import pytest
 import torch
 
