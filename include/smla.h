@@ -48,6 +48,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Entry points are the library's only exported symbols (it is built with
+ * hidden visibility for everything else). */
+#if defined(__GNUC__) || defined(__clang__)
+#define SMLA_API __attribute__((visibility("default")))
+#else
+#define SMLA_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -91,7 +99,7 @@ typedef struct {
  *   lse        fp32 [T, H]       out: natural-log LSE of the valid scores,
  *              WITHOUT the sink; -inf for a token with no valid slot
  */
-smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
                      const int32_t* topk_idxs, const int32_t* topk_length,
                      const float* attn_sink, void* o, float* lse, void* stream);
 
@@ -100,7 +108,7 @@ smla_status smla_fwd(const smla_dims* dims, const void* q, const void* kv,
  * workgroup per token and group of 64 or 128 heads) give fewer than 128
  * workgroups, i.e. decode and short chunks against long top-k rows; 0 when
  * no split is made (then smla_fwd_splitkv is smla_fwd). */
-size_t smla_fwd_splitkv_workspace_size(const smla_dims* dims);
+SMLA_API size_t smla_fwd_splitkv_workspace_size(const smla_dims* dims);
 
 /* The forward with split KV [cuDNN-FE #785 review thread: the SM90 tile
  * scheduler's grid of (blocks, heads x splits, batch)]: the 64-slot blocks
@@ -113,7 +121,7 @@ size_t smla_fwd_splitkv_workspace_size(const smla_dims* dims);
  * when it holds no split).  workspace: workspace_bytes of device memory,
  * 16-byte aligned, or NULL; used by this call only.  Arguments, outputs and
  * errors otherwise as smla_fwd. */
-smla_status smla_fwd_splitkv(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_fwd_splitkv(const smla_dims* dims, const void* q, const void* kv,
                              const int32_t* topk_idxs, const int32_t* topk_length,
                              const float* attn_sink, void* o, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
@@ -123,7 +131,7 @@ smla_status smla_fwd_splitkv(const smla_dims* dims, const void* q, const void* k
  *   o, dO      bf16 [T, H, d_v]
  *   delta      fp32 [T, H]  out: sum_c o[t,h,c] * dO[t,h,c]
  */
-smla_status smla_bwd_preprocess(const smla_dims* dims, const void* o, const void* dO,
+SMLA_API smla_status smla_bwd_preprocess(const smla_dims* dims, const void* o, const void* dO,
                                 float* delta, void* stream);
 
 /* Exact Delta, the high-accuracy alternative to smla_bwd_preprocess
@@ -139,7 +147,7 @@ smla_status smla_bwd_preprocess(const smla_dims* dims, const void* o, const void
  * Inputs: q, kv, topk_idxs, topk_length, attn_sink as in smla_fwd; dO bf16
  * [T, H, d_v]; lse fp32 [T, H] from smla_fwd.  No workspace.
  */
-smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const void* kv,
                                  const void* dO, const float* lse, const int32_t* topk_idxs,
                                  const int32_t* topk_length, const float* attn_sink,
                                  float* delta, void* stream);
@@ -150,13 +158,13 @@ smla_status smla_bwd_delta_exact(const smla_dims* dims, const void* q, const voi
  * (never less than what one token needs).  Returns 0 for unsupported sizes
  * as well; smla_bwd reports the error.  smla_bwd accepts any larger or
  * smaller workspace down to one token's need and sizes its chunks to it. */
-size_t smla_bwd_workspace_size(const smla_dims* dims);
+SMLA_API size_t smla_bwd_workspace_size(const smla_dims* dims);
 
 /* Tokens per chunk that smla_bwd uses with a workspace of workspace_bytes
  * (the largest chunk whose workspace fits, evened out over the chunks when
  * that fits too); 0 if not even one token's chunk fits (smla_bwd then
  * returns SMLA_ERR_WORKSPACE) or the sizes are unsupported. */
-int smla_bwd_chunk_tokens(const smla_dims* dims, size_t workspace_bytes);
+SMLA_API int smla_bwd_chunk_tokens(const smla_dims* dims, size_t workspace_bytes);
 
 /* Backward of L = sum(dO * O) [cuDNN-FE #785 Summary 1-3, Why 1-3;
  * cuDNN-FE #298].  Recomputes the probabilities from the forward's LSE and
@@ -188,7 +196,7 @@ int smla_bwd_chunk_tokens(const smla_dims* dims, size_t workspace_bytes);
  * SMLA_ERR_WORKSPACE if workspace is NULL or holds less than one token's
  * chunk.
  */
-smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const void* dO,
+SMLA_API smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const void* dO,
                      const float* lse, const float* delta, const int32_t* topk_idxs,
                      const int32_t* topk_length, const float* attn_sink, void* dq,
                      float* dkv, float* d_sink, void* workspace, size_t workspace_bytes,
@@ -205,7 +213,7 @@ smla_status smla_bwd(const smla_dims* dims, const void* q, const void* kv, const
  * Every other argument, output, the workspace and the errors are those of
  * smla_bwd; o must be non-NULL and 16-byte aligned when T > 0.
  */
-smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv,
                             const void* dO, const void* o, const float* lse, float* delta,
                             const int32_t* topk_idxs, const int32_t* topk_length,
                             const float* attn_sink, void* dq, float* dkv, float* d_sink,
@@ -227,7 +235,7 @@ smla_status smla_bwd_from_o(const smla_dims* dims, const void* q, const void* kv
  * created or destroyed, by the library).  Errors: SMLA_ERR_NULL for a NULL
  * array or handle, SMLA_ERR_SHAPE if n_events is too small, then as smla_bwd.
  */
-smla_status smla_bwd_profiled(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_bwd_profiled(const smla_dims* dims, const void* q, const void* kv,
                               const void* dO, const float* lse, const float* delta,
                               const int32_t* topk_idxs, const int32_t* topk_length,
                               const float* attn_sink, void* dq, float* dkv, float* d_sink,
@@ -255,14 +263,14 @@ smla_status smla_bwd_profiled(const smla_dims* dims, const void* q, const void* 
  * race; serialise them.  dkv's bits follow the chunk size, so they can differ
  * from smla_bwd's with a larger workspace by the summation grouping.
  */
-smla_status smla_bwd_noalloc(const smla_dims* dims, const void* q, const void* kv,
+SMLA_API smla_status smla_bwd_noalloc(const smla_dims* dims, const void* q, const void* kv,
                              const void* dO, const float* lse, const float* delta,
                              const int32_t* topk_idxs, const int32_t* topk_length,
                              const float* attn_sink, void* dq, float* dkv, float* d_sink,
                              void* stream);
 
 /* Static description of a status code. */
-const char* smla_status_string(smla_status status);
+SMLA_API const char* smla_status_string(smla_status status);
 
 #ifdef __cplusplus
 }

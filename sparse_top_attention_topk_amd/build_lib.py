@@ -23,6 +23,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-shared",
     "-Wall",
+    # host code: only the C entry points (marked SMLA_API in smla.h) leave
+    # the library
+    "-Xarch_host", "-fvisibility=hidden",
     # packed fp32 instructions are not emitted (the compiler may otherwise
     # form v_pk_* fp32 ops from scalar or float2 code)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

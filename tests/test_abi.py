@@ -22,7 +22,8 @@ def lib():
 
 def declared_functions():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:smla_status|size_t|int|const char\*)\s+(smla_\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:SMLA_API\s+)?(?:smla_status|size_t|int|const char\*)\s+(smla_\w+)\(",
+                                 src, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -42,6 +43,15 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib.LIB, name)
+
+
+def test_library_exports_no_other_functions(lib):
+    """The library's exported functions are the header's entry points: its
+    internal C++ functions (launchers, kernel stubs) stay hidden."""
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    functions = set(re.findall(r"^\S+ [TW] (\S+)$", out, re.M))
+    assert functions == set(declared_functions())
 
 
 def test_status_strings(lib):
