@@ -387,6 +387,79 @@ def test_batched_large_kv_set():
     assert not errors, "; ".join(errors)
 
 
+def largest_kv_problem(d_qk, S_kv, T=48, H=24, W=200, R=4000, seed=None):
+    """A problem over the largest KV set (S_kv rows) whose valid slots name R
+    of its rows: the first 500, the last 1500 and 2000 in between.  Returns
+    (p, rows, idx_big): p is the same problem over those R rows alone (row k
+    of p is KV row rows[k]; indices renumbered, slots in the same order), and
+    idx_big holds p's indices as KV rows of the large set, its padding -1 or
+    values >= S_kv (S_kv itself, S_kv + 7, 2^31 - 1).  Rows that no valid
+    slot names take no part in any output, so p's oracle results are the
+    large problem's (dKV: rows[k] <-> row k; every other row 0)."""
+    rng = np.random.default_rng(170 + d_qk if seed is None else seed)
+    mid = rng.choice(S_kv - 2000, size=R - 2000, replace=False) + 500
+    rows = np.sort(np.concatenate([np.arange(500), mid, np.arange(S_kv - 1500, S_kv)])).astype(np.int64)
+    assert len(np.unique(rows)) == R and rows[-1] == S_kv - 1
+    local = np.full((T, W), -1, dtype=np.int64)
+    for t in range(T):
+        n = int(rng.integers(W // 2, W + 1))
+        local[t, rng.choice(W, size=n, replace=False)] = rng.choice(R, size=n, replace=False)
+    local[0, 0], local[1, W - 1] = R - 1, 0                 # the last and the first row
+    big = np.where(local >= 0, rows[np.clip(local, 0, None)], -1)
+    pad = np.argwhere(local < 0)
+    bad = np.array([S_kv, S_kv + 7, 2 ** 31 - 1])
+    pick = pad[rng.random(len(pad)) < 0.3]
+    big[pick[:, 0], pick[:, 1]] = bad[rng.integers(0, 3, len(pick))]
+
+    def bf(shape, mul=1.0):
+        return torch.from_numpy((rng.standard_normal(size=shape) * mul).astype(np.float32)).to(torch.bfloat16)
+
+    p = wl.Problem(name=f"largest_kv_d{d_qk}", T=T, S_kv=R, H=H, d_qk=d_qk, d_v=512, W=W,
+                   scale=1.0 / np.sqrt(d_qk), q=bf((T, H, d_qk)), kv=bf((R, d_qk)), dO=bf((T, H, 512)),
+                   topk_idxs=torch.from_numpy(local.astype(np.int32)), topk_length=None,
+                   attn_sink=torch.from_numpy(rng.standard_normal(H).astype(np.float32)))
+    return p, rows, torch.from_numpy(big.astype(np.int32))
+
+
+@pytest.mark.parametrize("d_qk,S_kv", ((576, 1864135), (512, 2097151)))
+def test_largest_kv_set(d_qk, S_kv):
+    """The largest KV set the boundary accepts (KV rows are addressed with
+    32-bit byte offsets: S_kv * d_qk * 2 just under 2^31), with valid slots
+    on its first and last rows and padding values at and past S_kv, through
+    forward, preprocess and backward (48 tokens: the backward's split block
+    ranges): O, LSE, Delta, dQ and d_sink on every token, and dKV on every
+    named row, against the oracle on the same problem over the named rows
+    alone; every other dKV row exactly 0 (the outputs start as NaN)."""
+    from sparse_top_attention_topk_amd import _lib
+    p, rows, idx_big = largest_kv_problem(d_qk, S_kv)
+    say(f"[gpu] largest kv set: S_kv={S_kv} d_qk={d_qk} T={p.T} H={p.H} W={p.W} named rows={len(rows)}")
+    rows_d = torch.from_numpy(rows).to(DEV)
+    kv = torch.zeros((S_kv, d_qk), dtype=torch.bfloat16, device=DEV)
+    kv[rows_d] = p.kv.to(DEV)
+    q, dO, idx, sink = p.q.to(DEV), p.dO.to(DEV), idx_big.to(DEV), p.attn_sink.to(DEV)
+    o = torch.full((p.T, p.H, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((p.T, p.H), float("nan"), dtype=torch.float32, device=DEV)
+    dq = torch.full((p.T, p.H, d_qk), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dkv = torch.full((S_kv, d_qk), float("nan"), dtype=torch.float32, device=DEV)
+    d_sink = torch.full((p.H,), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = _lib.smla_fwd(q, kv, idx, None, sink, p.scale, o=o, lse=lse)
+    delta = _lib.smla_bwd_preprocess(o, dO)
+    dq, dkv, d_sink = _lib.smla_bwd(q, kv, dO, lse, delta, idx, None, sink, p.scale, dq=dq, dkv=dkv,
+                                    d_sink=d_sink)
+    named = torch.zeros((S_kv,), dtype=torch.bool, device=DEV)
+    named[rows_d] = True
+    stray = int(torch.count_nonzero((dkv != 0).any(dim=1) & ~named))
+    gpu = dict(o=o.float().cpu().numpy(), lse=lse.cpu().numpy(), dq=dq.float().cpu().numpy(),
+               delta=delta.cpu().numpy(), dkv=dkv[rows_d].cpu().numpy(), d_sink=d_sink.cpu().numpy())
+    del kv, dkv, named
+    ref = run_oracle(p)
+    errors = compare_full(gpu, ref)
+    check_tensor("delta", gpu["delta"], ref["delta"], errors)
+    if stray:
+        errors.append(f"dkv: {stray} rows that no valid slot names are not 0")
+    assert not errors, f"largest kv set d_qk={d_qk}: " + "; ".join(errors)
+
+
 # ---------------------------------------------------------------------------
 # few tokens: the blocks of each row split over several workgroups
 # ---------------------------------------------------------------------------
