@@ -1257,7 +1257,7 @@ __device__ __forceinline__ void dkv_block(const BwdArgs& a, const __bf16* pd, co
         const int slot = 16 * qt + n;
         const int v = raw[slot];
         if (b * BLK + slot < L && v >= 0 && v < a.S_kv) {
-            const int soff = (b * BLK + 16 * qt) * (2 * DQK);
+            const int soff = 16 * qt * (2 * DQK);         // prs starts at the block's first slot row
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{blk[0][0], blk[0][1], blk[1][0], blk[1][1]}, prs, voff,
                                                    soff, 0);
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{blk[2][0], blk[2][1], blk[3][0], blk[3][1]}, prs,
@@ -1387,18 +1387,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_kernel(BwdArgs a) {
         zero_rows_past_h(s_pd0);
     }
 
-    // ---- blocks: [P | dS] tiles double-buffered.  The token's partial rows
-    // (Wp rows of 2 d_qk bytes) through a buffer resource: lane (g, n) stores
-    // slot 16 qt + n, columns c_wave + 16g .. +15 (the main tiles, after the
-    // transpose) and c_rope + 4g .. +3 (its rope tile)
-    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK), (short)0, a.Wp * (2 * DQK),
-        0x00020000);
+    // ---- blocks: [P | dS] tiles double-buffered.  A block's partial rows
+    // (64 rows of 2 d_qk bytes) through a buffer resource based at the
+    // block's first row (64-bit address: a token's rows may span more than
+    // 2^31 bytes): lane (g, n) stores slot 16 qt + n, columns c_wave + 16g ..
+    // +15 (the main tiles, after the transpose) and c_rope + 4g .. +3 (its
+    // rope tile)
+    char* const part_t = reinterpret_cast<char*>(a.partial) + (size_t)(t - a.t0) * a.Wp * (2 * DQK);
     static_assert(MW == 4, "the block transpose takes four main column tiles per wave");
     const int voff = (lane & 15) * (2 * DQK) + 2 * (c_wave + 16 * (lane >> 4));
     const int voff_rope = (lane & 15) * (2 * DQK) + 2 * (c_rope + 4 * (lane >> 4));
     // one copy of the block per kind of wave, so the MFMAs stay in one basic block
     auto block = [&](const __bf16* pd, const int* raw, int b) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            part_t + (size_t)b * (BLK * 2 * DQK), (short)0, BLK * 2 * DQK, 0x00020000);
         if (has_rope)
             dkv_block<DQK, HK, MW, RW, RW != 0>(a, pd, raw, qB, dB, b, L, prs, voff, voff_rope, lane);
         else

@@ -421,6 +421,43 @@ def largest_kv_problem(d_qk, S_kv, T=48, H=24, W=200, R=4000, seed=None):
     return p, rows, torch.from_numpy(big.astype(np.int32))
 
 
+def partial_rows_past_2g_problem(T, W, S=2048, H=8, n_valid=1500, seed=None):
+    """Non-compact rows so wide that one token's dKV partial rows (W slots of
+    2 d_qk = 1152 bytes) span more than 2^31 bytes: n_valid distinct KV rows at
+    random slot positions over the whole width, -1 elsewhere; token 0 also
+    names the last slot and, when W reaches it, the first slot whose partial
+    row starts past 2^31 bytes.  A finite sink."""
+    rng = np.random.default_rng(180 + T if seed is None else seed)
+    d_qk = 576
+    idx = np.full((T, W), -1, dtype=np.int32)
+    for t in range(T):
+        pos = rng.choice(W, size=n_valid, replace=False)
+        idx[t, pos] = rng.choice(S, size=n_valid, replace=False)
+    first_past = -(-(2 ** 31) // (2 * d_qk))
+    idx[0, W - 1] = 5
+    if W > first_past:
+        idx[0, first_past] = 7
+
+    def bf(shape):
+        return torch.from_numpy(rng.standard_normal(size=shape).astype(np.float32)).to(torch.bfloat16)
+
+    return wl.Problem(name=f"partial_rows_past_2g_T{T}_W{W}", T=T, S_kv=S, H=H, d_qk=d_qk, d_v=512, W=W,
+                      scale=1.0 / np.sqrt(d_qk), q=bf((T, H, d_qk)), kv=bf((S, d_qk)), dO=bf((T, H, 512)),
+                      topk_idxs=torch.from_numpy(idx), topk_length=None,
+                      attn_sink=torch.from_numpy(rng.standard_normal(H).astype(np.float32)))
+
+
+@pytest.mark.parametrize("T,W", ((2, 2 ** 21 + 100), (1, 2 ** 24)))
+def test_partial_rows_past_2g(T, W):
+    """Rows whose dKV partial rows span more than 2^31 bytes per token, up to
+    the widest rows the boundary accepts (2^24 slots): every output against
+    the oracle (the partial rows are addressed per block from a 64-bit base)."""
+    p = partial_rows_past_2g_problem(T, W)
+    say(f"[gpu] partial rows past 2^31 bytes: T={T} W={W} S_kv={p.S_kv} H={p.H} valid={p.valid_count()}")
+    errors = compare_full(run_gpu(p, DEV), run_oracle(p))
+    assert not errors, f"partial rows past 2^31 bytes T={T} W={W}: " + "; ".join(errors)
+
+
 @pytest.mark.parametrize("d_qk,S_kv", ((576, 1864135), (512, 2097151)))
 def test_largest_kv_set(d_qk, S_kv):
     """The largest KV set the boundary accepts (KV rows are addressed with
