@@ -512,7 +512,7 @@ __device__ __forceinline__ BlockRange block_range(const BwdArgs& a, int L) {
 
 template <int DQK, int NW, typename Body, typename Post = NoPost, typename Early = NoPost>
 __device__ __forceinline__ void gathered_blocks(const BwdArgs& a, __bf16* s_tile0, __bf16* s_tile1,
-                                                int (*s_rows)[BLK], int* s_live, int* s_last, int t, int L, int nblk,
+                                                int (*s_rows)[BLK], int* s_live, int* s_last, int t, int nblk,
                                                 BlockRange rg, int wave, int lane, Body&& body, Post&& post = Post{},
                                                 Early&& early = Early{}) {
     const int b_lo = rg.b_lo, j_hi = rg.j_hi;
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(NW * 64, 1) void delta_exact_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) pdp[nt] = 0.f;
     const typename Tile::Lane TL = Tile::lane_bases(lane);
-    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
+    gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, nblk, block_range(a, L),
                              wave, lane,
                              [&](const __bf16* tile, const int* rows, int, const auto& gs, bool live) {
                                  if (active && live)
@@ -1047,7 +1047,7 @@ __global__ __launch_bounds__(256, 1) void bwd_sdq_kernel(BwdArgs a) {
             }
         };
         const typename Tile::Lane TL = Tile::lane_bases(lane);
-        gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, L, nblk, block_range(a, L),
+        gathered_blocks<DQK, NW>(a, s_tile0, s_tile1, s_rows, s_live, s_last, t, nblk, block_range(a, L),
                                  wave, lane,
                                  [&](const __bf16* tile, const int* rows, int b, const auto& gs, bool live) {
                                      if (active && live)
