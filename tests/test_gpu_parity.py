@@ -421,6 +421,21 @@ def largest_kv_problem(d_qk, S_kv, T=48, H=24, W=200, R=4000, seed=None):
     return p, rows, torch.from_numpy(big.astype(np.int32))
 
 
+@pytest.mark.parametrize("scale", (0.0, -1.0 / 24, 1e-30, 0.5, 2.0))
+def test_softmax_scales(scale):
+    """Finite scales away from 1/sqrt(d_qk), all inside the boundary's
+    contract: 0 (uniform weights), negative (the scores' order reversed), tiny,
+    and 12x / 48x the usual (scores spread over hundreds of nats, so that many
+    rows outgrow their first block's reference and the forward reruns them),
+    on DeepSeek-V4-like rows (window 64 + top-k 128, three blocks), H = 48,
+    compact and with a sink, against the oracle."""
+    p = wl.make_dsv4(160, 48, 576, 512, 128, seed=190, window=64, compact=True, scale=scale,
+                     name=f"scale_{scale:g}")
+    say(f"[gpu] softmax scale {scale:g}: T={p.T} H={p.H} W={p.W}")
+    errors = compare_full(run_gpu(p, DEV), run_oracle(p))
+    assert not errors, f"scale {scale:g}: " + "; ".join(errors)
+
+
 def partial_rows_past_2g_problem(T, W, S=2048, H=8, n_valid=1500, seed=None):
     """Non-compact rows so wide that one token's dKV partial rows (W slots of
     2 d_qk = 1152 bytes) span more than 2^31 bytes: n_valid distinct KV rows at
