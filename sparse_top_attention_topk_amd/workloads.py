@@ -499,12 +499,13 @@ def make_spiky_dsv4(T=4096, H=128, d_qk=576, topk=512, seed=2, frac=0.10, name=N
                    p.topk_idxs, None, p.attn_sink, meta=dict(p.meta, late_spike=late))
 
 
-def make_decode(T, S_kv=16384, H=128, d_qk=576, topk=1024, window=128, seed=110, name=None):
+def make_decode(T, S_kv=16384, H=128, d_qk=576, topk=1024, window=128, seed=110, name=None, scale=None):
     """Few query tokens at the end of a long KV set (decode, or a short
     prefill chunk): query i sits at position S_kv - T + i and holds the
     DeepSeek-V4-like [window | top-k] row of that position (the window of
     the <= 128 latest positions, then top-k distinct positions from before
-    the window), -1 padded.  d_v = 512, fp32 sink N(0, 1)."""
+    the window), -1 padded.  d_v = 512, fp32 sink N(0, 1); scale
+    1/sqrt(d_qk) unless given."""
     rng = np.random.default_rng(seed)
     q, kv, dO, s = _dense(rng, T, S_kv, H, d_qk, 512, True)
     W = window + topk
@@ -517,7 +518,7 @@ def make_decode(T, S_kv=16384, H=128, d_qk=576, topk=1024, window=128, seed=110,
         if k > 0:
             idx[i, window: window + k] = rng.choice(lo, size=k, replace=False)
     return Problem(name or f"decode_T{T}_S{S_kv}_H{H}_k{topk}", T, S_kv, H, d_qk, 512, W,
-                   1.0 / math.sqrt(d_qk), q, kv, dO, torch.from_numpy(idx), None, s,
+                   1.0 / math.sqrt(d_qk) if scale is None else scale, q, kv, dO, torch.from_numpy(idx), None, s,
                    meta=dict(seed=seed, window=window, topk=topk))
 
 

@@ -26,6 +26,17 @@ REL_TOL = 2e-2
 COS_MIN = 0.9995
 LSE_TOL = 1e-3
 DSINK_TOL = 1e-2
+# Outputs are fp32 and the kernels' fp32 exponentials return no subnormal
+# results: a d_sink reference below the smallest normal fp32 is 0 at the
+# kernel's precision.
+FP32_TINY = float(np.finfo(np.float32).tiny)
+# Whether a dKV row is nonzero is decided at the kernel's precision: P below
+# 2^-126 is 0 there, and the 16-bit partials keep each slot's contribution to
+# 2^-127 absolute, so a row whose reference lies wholly below 2^26 such
+# contributions (more slots than any problem here names one row with) may be
+# exactly 0; only rows above that, and rows the reference leaves exactly 0,
+# are decided.
+DKV_ROW_FLOOR = 2.0 ** -100
 
 
 def say(*a):
@@ -199,6 +210,7 @@ def check_dsink(gpu, ref, errors):
     if gpu is None or not np.all(np.isfinite(gpu)):
         errors.append("d_sink: missing or non-finite")
         return
+    ref = np.where(np.abs(ref) < FP32_TINY, 0.0, ref)
     m = np.abs(ref).max()
     e = np.abs(gpu - ref).max()
     if (m == 0 and e > 1e-6) or (m > 0 and e > DSINK_TOL * m):
@@ -206,10 +218,15 @@ def check_dsink(gpu, ref, errors):
 
 
 def check_dkv_rows(gpu_dkv, ref_dkv, errors):
+    """Rows the reference leaves exactly 0 are exactly 0; rows whose reference
+    reaches DKV_ROW_FLOOR are nonzero; rows in between are not decided."""
     g = np.any(gpu_dkv != 0, axis=1)
-    r = np.any(ref_dkv.astype(np.float32) != 0, axis=1)
-    if not np.array_equal(g, r):
-        errors.append(f"dkv rows: nonzero row sets differ ({np.count_nonzero(g != r)} rows)")
+    m = np.abs(ref_dkv).max(axis=1)
+    decided = (m == 0) | (m >= DKV_ROW_FLOOR)
+    r = m >= DKV_ROW_FLOOR
+    bad = decided & (g != r)
+    if np.any(bad):
+        errors.append(f"dkv rows: nonzero row sets differ ({np.count_nonzero(bad)} rows)")
 
 
 def compare_exact_delta(gpu, ref64, errors):

@@ -523,6 +523,8 @@ SPLIT_CASES = {
     "decode-T5-h24-k2048": lambda: wl.make_decode(5, S_kv=8192, H=24, topk=2048, seed=141),
     "spiky-T96-h64": lambda: wl.make_spiky(64, T=96, window=32, topk=160, frac=0.5),
     "decode-T1-k8064": lambda: wl.make_decode(1, H=128, topk=8064, seed=142),   # 128 blocks: 64 splits
+    # scores spread over hundreds of nats: block ranges rerun with their own exact max
+    "decode-T16-h64-scale2": lambda: wl.make_decode(16, S_kv=4096, H=64, seed=143, scale=2.0),
     "edge-wide-h128-T64": lambda: wl.make_edge_wide(128, T=64),
 }
 
