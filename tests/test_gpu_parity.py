@@ -421,6 +421,35 @@ def largest_kv_problem(d_qk, S_kv, T=48, H=24, W=200, R=4000, seed=None):
     return p, rows, torch.from_numpy(big.astype(np.int32))
 
 
+def lengths_out_of_range_problem(T=128):
+    """The compact edge problem (H = 24, W = 64) with lengths outside [0, W]
+    on its first tokens: -1, -2^31, W + 1, 2^31 - 1, then 0 and W (clamped
+    to [0, W]: empty, empty, full, full); ``T`` < 128 keeps the first T
+    tokens (split block ranges and the one-workgroup index inversion)."""
+    p = wl.make_edge_compact(24)
+    ln = p.topk_length.numpy().copy()
+    ln[:6] = [-1, -2 ** 31, p.W + 1, 2 ** 31 - 1, 0, p.W]
+    return wl.Problem(f"lengths_out_of_range_T{T}", T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale, p.q[:T],
+                      p.kv, p.dO[:T], p.topk_idxs[:T], torch.from_numpy(ln[:T].copy()), p.attn_sink)
+
+
+@pytest.mark.parametrize("T", (128, 16))
+def test_lengths_out_of_range(T):
+    """Compact lengths below 0 and above W, up to the int32 extremes, are
+    clamped to [0, W] by every kernel that reads them (forward, backward,
+    index inversion; with 16 tokens the split paths), against the oracle."""
+    p = lengths_out_of_range_problem(T)
+    say(f"[gpu] lengths out of range: T={p.T} W={p.W} lengths {p.topk_length[:6].tolist()}")
+    gpu = run_gpu(p, DEV)
+    errors = compare_full(gpu, run_oracle(p))
+    if T < 128:
+        _, o_s, lse_s = _fwd_split(p)
+        ref = run_oracle(p)
+        check_tensor("o (split fwd)", o_s, ref["o"], errors)
+        check_lse(lse_s, ref["lse"], errors)
+    assert not errors, f"lengths out of range T={T}: " + "; ".join(errors)
+
+
 @pytest.mark.parametrize("scale", (0.0, -1.0 / 24, 1e-30, 0.5, 2.0))
 def test_softmax_scales(scale):
     """Finite scales away from 1/sqrt(d_qk), all inside the boundary's
