@@ -429,14 +429,22 @@ def lengths_out_of_range_problem(T=128):
     p = wl.make_edge_compact(24)
     ln = p.topk_length.numpy().copy()
     ln[:6] = [-1, -2 ** 31, p.W + 1, 2 ** 31 - 1, 0, p.W]
+    # tokens 6..9: invalid values inside the row's length (slots that do not
+    # count), -1, -5, S_kv and 2^31 - 1 at every third slot
+    idx = p.topk_idxs.numpy().copy()
+    for k, t in enumerate(range(6, 10)):
+        ln[t] = p.W
+        idx[t, k::3] = (-1, -5, p.S_kv, 2 ** 31 - 1)[k]
     return wl.Problem(f"lengths_out_of_range_T{T}", T, p.S_kv, p.H, p.d_qk, p.d_v, p.W, p.scale, p.q[:T],
-                      p.kv, p.dO[:T], p.topk_idxs[:T], torch.from_numpy(ln[:T].copy()), p.attn_sink)
+                      p.kv, p.dO[:T], torch.from_numpy(idx[:T].copy()), torch.from_numpy(ln[:T].copy()),
+                      p.attn_sink)
 
 
 @pytest.mark.parametrize("T", (128, 16))
 def test_lengths_out_of_range(T):
     """Compact lengths below 0 and above W, up to the int32 extremes, are
-    clamped to [0, W] by every kernel that reads them (forward, backward,
+    clamped to [0, W] by every kernel that reads them, and invalid values
+    inside a row's length are slots that do not count (forward, backward,
     index inversion; with 16 tokens the split paths), against the oracle."""
     p = lengths_out_of_range_problem(T)
     say(f"[gpu] lengths out of range: T={p.T} W={p.W} lengths {p.topk_length[:6].tolist()}")
