@@ -421,6 +421,52 @@ def largest_kv_problem(d_qk, S_kv, T=48, H=24, W=200, R=4000, seed=None):
     return p, rows, torch.from_numpy(big.astype(np.int32))
 
 
+def test_tokens_past_2g_elements():
+    """T = 32768 tokens at H = 128, d_qk = 576 (DeepSeek-V4-like rows, window
+    128 + top-k 512): q, dO, O and dQ hold more than 2^31 elements, so the
+    rows of the last ~3600 tokens start past 32-bit element offsets.  q, kv
+    and dO are drawn on the GPU from a seeded generator.  O, LSE, Delta and dQ
+    of sampled tokens (among them the first past 2^31 elements and the last),
+    and dKV of rows near the end (every token that names them included),
+    against the oracle on those tokens."""
+    from sparse_top_attention_topk_amd import _lib
+    T, H, d_qk = 32768, 128, 576
+    assert T * H * d_qk > 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(210)
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+
+    q, kv, dO = draw((T, H, d_qk)), draw((T, d_qk)), draw((T, H, 512))
+    sink = torch.randn((H,), generator=g, device=DEV, dtype=torch.float32)
+    idx_np = wl._window_topk_idxs(np.random.default_rng(210), T, 128, 512)
+    idx = torch.from_numpy(idx_np).to(DEV)
+    scale = 1.0 / np.sqrt(d_qk)
+    say(f"[gpu] tokens past 2^31 elements: T={T} H={H} d_qk={d_qk} (q: {T * H * d_qk} elements)")
+    o, lse = _lib.smla_fwd(q, kv, idx, None, sink, scale)
+    delta = _lib.smla_bwd_preprocess(o, dO)
+    dq, dkv, _ = _lib.smla_bwd(q, kv, dO, lse, delta, idx, None, sink, scale)
+    torch.cuda.synchronize()
+    first_past = -(-(2 ** 31) // (H * d_qk))
+    rows = np.array([T - 1, T - 130, T - 300])
+    valid = (idx_np >= 0) & (idx_np < T)
+    namers = np.nonzero((valid & np.isin(idx_np, rows)).any(axis=1))[0]
+    sampled = np.array([0, 1, 640, first_past - 1, first_past, first_past + 1, T - 2, T - 1])
+    toks = np.unique(np.concatenate([sampled, namers]))
+    tk = torch.from_numpy(toks).to(DEV)
+    p = wl.Problem("tokens_past_2g_subset", len(toks), T, H, d_qk, 512, idx_np.shape[1], scale,
+                   q[tk].cpu(), kv.cpu(), dO[tk].cpu(), torch.from_numpy(idx_np[toks]), None, sink.cpu())
+    ref = run_oracle(p)
+    errors = []
+    check_tensor("o[sampled]", o[tk].float().cpu().numpy(), ref["o"], errors)
+    check_lse(lse[tk].cpu().numpy(), ref["lse"], errors)
+    check_tensor("dq[sampled]", dq[tk].float().cpu().numpy(), ref["dq"], errors)
+    check_tensor("delta[sampled]", delta[tk].cpu().numpy(), ref["delta"], errors)
+    check_tensor("dkv[rows near the end]", dkv[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref["dkv"][rows],
+                 errors)
+    assert not errors, "tokens past 2^31 elements: " + "; ".join(errors)
+
+
 def lengths_out_of_range_problem(T=128):
     """The compact edge problem (H = 24, W = 64) with lengths outside [0, W]
     on its first tokens: -1, -2^31, W + 1, 2^31 - 1, then 0 and W (clamped
